@@ -1,0 +1,234 @@
+/*
+ * rkv.h -- C ABI of librkv, the MI355X (gfx950) library for RocketKV's decode
+ * path: SnapKV++ stage-1 eviction once per prefill, then Hybrid Sparse
+ * Attention (HSA) over the pruned, paged KV cache at every decode step.
+ *
+ * Sources (web pages on RocketKV, cited by title and section):
+ *   [P1] "RocketKV: Accelerating Long-Context LLM Inference via Two-Stage KV
+ *        Cache Compression" (atlas.scime.ai summary): "Approach".
+ *   [P2] The paper's abstract (papers.pytorch.kr/papers/2502.14051).
+ *   [P3] "RocketKV-adapted -- Two-Stage Compression" (veloxquant-mlx docs):
+ *        "Where it sits -- the mechanism gap", "The one setting worth
+ *        tuning", "Adaptation notes", "Evidence".
+ *
+ * Conventions shared by every entry point
+ *  - Device pointers are HIP device addresses (for example torch CUDA tensor
+ *    data pointers); host pointers are marked "host".  The caller owns every
+ *    buffer; the library allocates nothing and keeps no mutable global state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work on it; nothing synchronises the host.  Calls on
+ *    different streams are independent as long as their buffers are.
+ *  - Every call returns an rkv status (0 = RKV_OK).  Arguments are checked on
+ *    the host before anything is enqueued; a failed check enqueues nothing.
+ *    Values that live in device memory (sequence lengths, page tables) cannot
+ *    be checked on the host: kernels clamp them so that no access leaves the
+ *    buffers described here (a length is clamped to the cache capacity, a
+ *    page whose physical block is outside [0, num_blocks) is treated as
+ *    empty); results for such inputs are defined but meaningless.
+ *  - Element type `dtype` (RKV_F32 or RKV_BF16) applies to queries, keys,
+ *    values and page summaries alike.  Attention outputs are always fp32.
+ *  - GQA: query head h*G + j (j < G) reads KV head h.
+ *  - Index outputs are ascending and padded with -1.
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define RKV_OK 0
+#define RKV_EINVAL (-1)       /* bad argument (null pointer, out-of-range size) */
+#define RKV_EWORKSPACE (-2)   /* workspace missing or smaller than required */
+#define RKV_ECAPACITY (-3)    /* rows do not fit the cache / page table */
+#define RKV_EUNSUPPORTED (-4) /* shape or dtype this build has no kernel for */
+#define RKV_EHIP (-5)         /* a HIP launch reported an error */
+
+/* ---- element types ----------------------------------------------------- */
+#define RKV_F32 0
+#define RKV_BF16 1
+
+/* Supported shapes: head_dim in {64, 128}; group in {1, 2, 4, 8};
+ * page_size in [1, 256]; 1 <= k1 <= head_dim; 1 <= k2 <= RKV_MAX_K2. */
+#define RKV_MAX_K2 1024
+#define RKV_MAX_EVICT_BATCH 128
+
+/* GQA layout: Hq = n_kv_heads * group query heads. */
+typedef struct rkv_gqa {
+    int32_t n_kv_heads; /* Hkv */
+    int32_t group;      /* G */
+    int32_t head_dim;   /* d */
+} rkv_gqa;
+
+/* Paged KV cache.  A physical block holds one page of every KV head:
+ *   k_pool, v_pool : [num_blocks][Hkv][page_size][d]  (dtype)
+ *   page_table     : [B][max_pages] int32, physical block of logical page p
+ *                    of sequence b.
+ * Logical row r of sequence b, KV head h lives at
+ *   pool[page_table[b][r / page_size]][h][r % page_size][:].
+ * The page size is also HSA's page: summaries and page selection are per
+ * logical page.  Pools must be 16-byte aligned. */
+typedef struct rkv_paged_cache {
+    void *k_pool;
+    void *v_pool;
+    const int32_t *page_table;
+    int64_t num_blocks;
+    int32_t page_size; /* P */
+    int32_t max_pages; /* capacity per sequence = max_pages * P rows */
+} rkv_paged_cache;
+
+/* Page summaries ("summaries" below): [B][Hkv][2][d][max_pages] in dtype.
+ * [..][0][c][p] is the element-wise maximum and [..][1][c][p] the minimum of
+ * channel c over the valid rows of logical page p ([P3] "Where it sits":
+ * Quest-style paged max/min along the sequence).  Channel-major so that each
+ * selected channel is one contiguous run over the pages.  Among equal values
+ * the earliest row's bits are kept, so an incremental append gives the same
+ * bits as a rebuild ([P3] "Evidence"). */
+
+/* Human-readable text for a status code (static storage). */
+const char *rkv_status_string(int status);
+
+/* Content hash of the sources this library was built from (static storage). */
+const char *rkv_build_id(void);
+
+/* ---- adaptive split (host only) ---------------------------------------- */
+/* [P3] "The one setting worth tuning"; [P1] "Approach".
+ * r = clip(0.2 + 0.06 * log2(c), 0.2, 0.8); stage 1 keeps a 1/c^r share,
+ * stage 2 attends a 1/c^(1-r) share of what stage 1 kept.
+ *   c  : overall target compression ratio, finite and >= 1.
+ *   L  : prompt length (rows), >= 0;  w : observation window, >= 0.
+ *   keep = min(L, max(w, floor(L / c^r))).
+ * Any output pointer may be NULL.  Errors: RKV_EINVAL for c < 1, non-finite
+ * c, L < 0 or w < 0.  Pure host arithmetic in double precision. */
+int rkv_split_ratio(double c, int64_t L, int64_t w, double *r, double *c_evict,
+                    double *c_hsa, int64_t *keep);
+
+/* ---- SnapKV++ stage-1 eviction ------------------------------------------ */
+/* [P2] abstract: SnapKV++ = SnapKV with adaptive pooling size and full GQA
+ * compatibility.  [P1] "Approach": large pooling kernel, GQA-group-level
+ * selection.  Per sequence b and KV head h, with L = prompt_lens[b]:
+ *   - the last w prompt queries of the G heads of the group score every key
+ *     they can see (causal): p = softmax(scale * q . k) per query;
+ *   - the probabilities are summed over the window queries and then over
+ *     the G heads, for the prefix keys t < L - w;
+ *   - the sums are max-pooled with an odd window `pool_kernel` (centred,
+ *     stride 1, clipped at the ends of the prefix);
+ *   - the keep[b] - w best prefix keys (ties to the lower position) are
+ *     kept in ascending order, followed by the w window rows;
+ *   - K and V rows of the kept positions are written, in that order, to
+ *     logical rows [0, keep[b]) of sequence b in the paged cache.
+ * If keep[b] >= L every row is kept in place (no scoring).
+ * The softmax denominator is accumulated in fp64 and rounded once to fp32;
+ * everything else is fp32 with bf16 inputs widened exactly.
+ *
+ * Arguments
+ *   g, dtype      : GQA layout and element type.
+ *   B             : sequences, 1..RKV_MAX_EVICT_BATCH.
+ *   prompt_lens   : host [B], 0 <= L <= L_max.
+ *   keep          : host [B], rows to keep; w <= keep unless keep >= L.
+ *   L_max, w      : prompt row stride of q/k/v and observation window (>= 1).
+ *   pool_kernel   : odd, >= 1.
+ *   scale         : logit scale (normally 1/sqrt(d)), finite and > 0.
+ *   q_win         : device [B][Hq][w][d], query i of a head sits at L-w+i.
+ *   k, v          : device [B][Hkv][L_max][d], prompt keys/values (keys
+ *                   already position-encoded), 16-byte aligned.
+ *   cache         : destination; needs min(keep, L) <= max_pages * P.
+ *   summaries     : device, optional (NULL = skip); rebuilt for the kept
+ *                   rows [0, min(keep, L)) of every sequence.
+ *   kept_idx      : device [B][Hkv][keep_stride], optional; kept prompt
+ *                   positions, ascending, -1 padded.
+ *   keep_stride   : row stride of kept_idx; >= max_b min(keep[b], L_b).
+ *   pooled_scores : device [B][Hkv][L_max] fp32, optional; pooled score of
+ *                   every prefix key (entries >= L-w are left untouched).
+ *   seq_lens_out  : device [B] int32, optional; receives min(keep, L).
+ *   ws, ws_bytes  : device workspace of at least
+ *                   rkv_prefill_evict_workspace_bytes(g, B, L_max, w).
+ * Errors: RKV_EINVAL, RKV_EUNSUPPORTED, RKV_ECAPACITY, RKV_EWORKSPACE,
+ * RKV_EHIP. */
+size_t rkv_prefill_evict_workspace_bytes(const rkv_gqa *g, int32_t B, int64_t L_max,
+                                         int32_t w);
+int rkv_prefill_evict(const rkv_gqa *g, int32_t dtype, int32_t B,
+                      const int32_t *prompt_lens, const int32_t *keep, int64_t L_max,
+                      int32_t w, int32_t pool_kernel, float scale, const void *q_win,
+                      const void *k, const void *v, const rkv_paged_cache *cache,
+                      void *summaries, int32_t *kept_idx, int32_t keep_stride,
+                      float *pooled_scores, int32_t *seq_lens_out, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* ---- incremental page-summary append ------------------------------------ */
+/* [P3] "Where it sits" (paged max/min) and "Evidence" (incremental update
+ * == rebuild).  For every sequence b, rows [n_old[b], n_new[b]) are folded
+ * into the summaries of the pages they fall in.  A page that begins at or
+ * after n_old[b] is initialised from its first new row.  If k_src/v_src are
+ * given, the new rows are first copied into the paged cache from
+ *   k_src, v_src : device [B][Hkv][max_new_rows][d] (row r at index r-n_old).
+ * n_old, n_new  : device [B] int32; rows beyond n_old + max_new_rows and
+ *                 beyond the cache capacity are ignored; n_new <= n_old is a
+ *                 no-op for that sequence.
+ * max_new_rows  : >= 1, host-side bound on n_new - n_old (sizes the grid).
+ * summaries     : device [B][Hkv][2][d][max_pages].
+ * Errors: RKV_EINVAL, RKV_EUNSUPPORTED, RKV_EHIP. */
+int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,
+                         const rkv_paged_cache *cache, const int32_t *n_old,
+                         const int32_t *n_new, int32_t max_new_rows, const void *k_src,
+                         const void *v_src, void *summaries, void *stream);
+
+/* ---- Hybrid Sparse Attention decode ------------------------------------- */
+/* [P3] "Where it sits": scores are approximated by a two-dimensional
+ * reduction, SparQ-style top-magnitude channels along the head dimension and
+ * Quest-style page summaries along the sequence.  [P3] "Adaptation notes":
+ * whole pages (k2 of them) are selected.  [P3] "Evidence": the page score
+ * bounds every in-page dot product.  Per sequence b and KV head h with
+ * n = seq_lens[b] rows (NP = ceil(n/P) pages):
+ *   a[c]   = sum_j |q_j[c]|                         (fp32, j ascending)
+ *   I1     = k1 channels with the largest a (ties: lower c), ascending
+ *   s_j(p) = sum_{c in I1 asc} max(q_j[c]*Kmax[p][c], q_j[c]*Kmin[p][c])
+ *   S(p)   = sum_{j asc} s_j(p)                      (fp32, no fused mul-add)
+ *   I2     = min(k2, NP) pages with the largest S (ties: lower p), ascending
+ *   out_j  = softmax(scale * q_j . k_t) v_t over the valid rows t of the
+ *            pages in I2, fp32 accumulation.
+ * n = 0 selects nothing and writes zeros.
+ *
+ * Arguments
+ *   q            : device [B][Hq][d] decode queries.
+ *   seq_lens     : device [B] int32 rows per sequence (current token
+ *                  included); clamped to [0, max_pages * P].
+ *   summaries    : device [B][Hkv][2][d][max_pages], current for seq_lens.
+ *   k1, k2       : channels and pages kept.
+ *   chan_idx     : device [B][Hkv][k1] int32, optional.
+ *   page_idx     : device [B][Hkv][k2] int32 (required by rkv_hsa_select and
+ *                  rkv_hsa_attend, optional for rkv_hsa_decode).
+ *   page_scores  : device [B][Hkv][max_pages] fp32, optional; S(p) for
+ *                  p < NP (entries beyond are untouched).
+ *   scale        : logit scale (normally 1/sqrt(d)), finite and > 0.
+ *   out          : device [B][Hq][d] fp32.
+ *   ws, ws_bytes : device workspace of at least rkv_hsa_workspace_bytes(...)
+ *                  for the same shapes.
+ * rkv_hsa_decode = rkv_hsa_select followed by rkv_hsa_attend on `stream`.
+ * Errors: RKV_EINVAL, RKV_EUNSUPPORTED, RKV_EWORKSPACE, RKV_EHIP. */
+size_t rkv_hsa_workspace_bytes(const rkv_gqa *g, int32_t B, int32_t page_size,
+                               int32_t max_pages, int32_t k1, int32_t k2);
+int rkv_hsa_select(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
+                   const int32_t *seq_lens, int32_t page_size, int32_t max_pages,
+                   const void *summaries, int32_t k1, int32_t k2, int32_t *chan_idx,
+                   int32_t *page_idx, float *page_scores, void *ws, size_t ws_bytes,
+                   void *stream);
+int rkv_hsa_attend(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
+                   const rkv_paged_cache *cache, const int32_t *seq_lens,
+                   const int32_t *page_idx, int32_t k2, float scale, float *out, void *ws,
+                   size_t ws_bytes, void *stream);
+int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
+                   const rkv_paged_cache *cache, const int32_t *seq_lens,
+                   const void *summaries, int32_t k1, int32_t k2, float scale, float *out,
+                   int32_t *chan_idx, int32_t *page_idx, float *page_scores, void *ws,
+                   size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* RKV_H */

@@ -1,0 +1,325 @@
+// evict.hip -- SnapKV++ stage-1 eviction, once per prefill.
+//
+// The paper's abstract describes SnapKV++ as SnapKV with adaptive pooling
+// size and full grouped-query-attention compatibility; the atlas.scime.ai
+// summary ("Approach") adds that it uses a large pooling kernel and selects
+// at the GQA-group level.  Per (sequence, KV head):
+//   1. logits  : z = fl(sum_c fl(q[c] k[c])) * scale for the R = G*w window
+//                query rows against every prompt key (causal per row);
+//   2. softmax : row max m (exact), denominator ell accumulated in fp64 and
+//                rounded once to fp32, p = expf(z - m) / ell;
+//   3. scores  : A[t] = sum_j (sum_i p_{j,i}[t]) for the prefix t < L-w, in
+//                the same order and precision as the definition;
+//   4. pooling : max over a centred odd window, clipped at the prefix ends;
+//   5. keep    : top (keep - w) by (pooled desc, t asc), ascending, plus the
+//                w window rows;
+//   6. compact : gather K/V rows into the paged cache; rebuild summaries.
+// The logits are computed with one thread per query row walking an LDS tile
+// of keys in channel order without multiply-add contraction, so they match a
+// sequential fp32 evaluation bit for bit; only expf may differ from another
+// library's in the last place.
+//
+// Workspace (per call): logits Z[B][Hkv][L_max][R] fp32 (row-fastest so that
+// every pass reads it coalesced), per-tile row maxima, fp64 partial sums,
+// scores A, pooled scores and kept positions.
+#include "rkv_internal.h"
+
+namespace rkv {
+namespace {
+
+constexpr int kTK = 64;      // keys per logits tile
+constexpr int kCH = 512;     // keys per denominator chunk
+constexpr int kLogitsBlock = 128;
+
+struct EvictWs {
+    size_t z, tm, m, ell, pl, a, pooled, kept, nold, nnew, total;
+    int R, ntiles, nch;
+};
+
+EvictWs evict_layout(const rkv_gqa &g, int B, int64_t L_max, int w) {
+    EvictWs l;
+    l.R = g.group * w;
+    l.ntiles = (int)((L_max + kTK - 1) / kTK);
+    l.nch = (int)((L_max + kCH - 1) / kCH);
+    const size_t u = (size_t)B * g.n_kv_heads;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += align_up(bytes);
+        return at;
+    };
+    l.z = take(u * L_max * l.R * sizeof(float));
+    l.tm = take(u * l.ntiles * l.R * sizeof(float));
+    l.m = take(u * l.R * sizeof(float));
+    l.ell = take(u * l.R * sizeof(float));
+    l.pl = take(u * l.nch * l.R * sizeof(double));
+    l.a = take(u * L_max * sizeof(float));
+    l.pooled = take(u * L_max * sizeof(float));
+    l.kept = take(u * L_max * sizeof(int32_t));
+    l.nold = take((size_t)B * sizeof(int32_t));
+    l.nnew = take((size_t)B * sizeof(int32_t));
+    l.total = off;
+    return l;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kLogitsBlock)
+logits_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, const T *q_win, const T *k,
+              float scale, int ntiles, float *Z, float *TM) {
+    __shared__ float ks[kTK][D];
+    const int b = blockIdx.z, h = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
+    const int64_t L = seq.L[b];
+    if (seq.keep[b] >= L) return;
+    const int64_t t0 = (int64_t)tile * kTK;
+    if (t0 >= L) return;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int nk = (int)min<int64_t>(kTK, L - t0);
+    const T *kb = k + (bh * L_max + t0) * D;
+    for (int i = tid; i < kTK * D; i += kLogitsBlock) {
+        const int tt = i / D;
+        ks[tt][i % D] = tt < nk ? Elem<T>::ld(kb, i) : 0.0f;
+    }
+    __syncthreads();
+    for (int r = tid; r < R; r += kLogitsBlock) {
+        float qr[D];
+        const T *qp = q_win + (bh * R + r) * D;
+#pragma unroll
+        for (int c = 0; c < D; ++c) qr[c] = Elem<T>::ld(qp, c);
+        const int64_t last = L - w + (r % w);
+        float tmax = -INFINITY;
+        for (int tt = 0; tt < nk; ++tt) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int c = 0; c < D; ++c) dot = dot + qr[c] * ks[tt][c];
+            const float z = dot * scale;
+            Z[(bh * L_max + t0 + tt) * R + r] = z;
+            if (t0 + tt <= last) tmax = fmaxf(tmax, z);
+        }
+        TM[(bh * ntiles + tile) * R + r] = tmax;
+    }
+}
+
+__global__ void __launch_bounds__(256)
+rowmax_kernel(int Hkv, int R, EvictSeq seq, int ntiles, const float *TM, float *M) {
+    const int b = blockIdx.y, h = blockIdx.x;
+    const int64_t L = seq.L[b];
+    if (seq.keep[b] >= L) return;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int nt = (int)((L + kTK - 1) / kTK);
+    for (int r = threadIdx.x; r < R; r += 256) {
+        float m = -INFINITY;
+        for (int t = 0; t < nt; ++t) m = fmaxf(m, TM[(bh * ntiles + t) * R + r]);
+        M[bh * R + r] = m;
+    }
+}
+
+__global__ void __launch_bounds__(256)
+rowsum_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, int nch, const float *Z,
+              const float *M, double *PL) {
+    const int b = blockIdx.z, h = blockIdx.y, ch = blockIdx.x;
+    const int64_t L = seq.L[b];
+    if (seq.keep[b] >= L) return;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int64_t t0 = (int64_t)ch * kCH;
+    const int64_t t1 = min<int64_t>(L, t0 + kCH);
+    for (int r = threadIdx.x; r < R; r += 256) {
+        const int64_t last = L - w + (r % w);
+        const int64_t te = min<int64_t>(t1, last + 1);
+        const float mr = M[bh * R + r];
+        double acc = 0.0;
+        for (int64_t t = t0; t < te; ++t) acc += (double)expf(Z[(bh * L_max + t) * R + r] - mr);
+        PL[(bh * nch + ch) * R + r] = acc;
+    }
+}
+
+__global__ void __launch_bounds__(256)
+rowsum_final_kernel(int Hkv, int R, EvictSeq seq, int nch, const double *PL, float *ell) {
+    const int b = blockIdx.y, h = blockIdx.x;
+    const int64_t L = seq.L[b];
+    if (seq.keep[b] >= L) return;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    for (int r = threadIdx.x; r < R; r += 256) {
+        double acc = 0.0;
+        for (int c = 0; c < nch; ++c) acc += PL[(bh * nch + c) * R + r];
+        ell[bh * R + r] = (float)acc;
+    }
+}
+
+__global__ void __launch_bounds__(256)
+colsum_kernel(int Hkv, int G, int w, int64_t L_max, EvictSeq seq, const float *Z,
+              const float *M, const float *ell, float *A) {
+    extern __shared__ float sm[];
+    const int R = G * w;
+    float *Ms = sm, *Es = sm + R;
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int64_t L = seq.L[b];
+    if (seq.keep[b] >= L) return;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    for (int r = threadIdx.x; r < R; r += 256) {
+        Ms[r] = M[bh * R + r];
+        Es[r] = ell[bh * R + r];
+    }
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= L - w) return;
+    const float *zr = Z + (bh * L_max + t) * R;
+    float a = 0.0f;
+    for (int j = 0; j < G; ++j) {
+        float aj = 0.0f;
+        for (int i = 0; i < w; ++i) {
+            const int r = j * w + i;
+            const float p = expf(zr[r] - Ms[r]) / Es[r];
+            aj = aj + p;
+        }
+        a = a + aj;
+    }
+    A[bh * L_max + t] = a;
+}
+
+__global__ void __launch_bounds__(256)
+maxpool_kernel(int Hkv, int w, int64_t L_max, EvictSeq seq, int half, const float *A,
+            float *pooled) {
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int64_t L = seq.L[b];
+    if (seq.keep[b] >= L) return;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int64_t npre = L - w;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= npre) return;
+    const int64_t u0 = max<int64_t>(0, t - half), u1 = min<int64_t>(npre - 1, t + half);
+    const float *a = A + bh * L_max;
+    float best = a[u0];
+    for (int64_t u = u0 + 1; u <= u1; ++u) best = fmaxf(best, a[u]);
+    pooled[bh * L_max + t] = best;
+}
+
+constexpr int kKeepBlock = 1024;
+
+__global__ void __launch_bounds__(kKeepBlock)
+keep_kernel(int Hkv, int w, int64_t L_max, EvictSeq seq, const float *pooled, int32_t *kept,
+            int64_t kept_stride, int32_t *nold, int32_t *nnew, int32_t *seq_lens_out) {
+    __shared__ uint32_t hist[256];
+    __shared__ int wave_tot[kKeepBlock / kWave];
+    __shared__ int sh[2];
+    const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+    const int64_t L = seq.L[b];
+    const int64_t keep_eff = min<int64_t>(seq.keep[b], L);
+    const int64_t bh = (int64_t)b * Hkv + h;
+    int32_t *kp = kept + bh * kept_stride;
+    if (h == 0 && tid == 0) {
+        nold[b] = 0;
+        nnew[b] = (int32_t)keep_eff;
+        if (seq_lens_out) seq_lens_out[b] = (int32_t)keep_eff;
+    }
+    if (seq.keep[b] >= L) {
+        for (int64_t i = tid; i < kept_stride; i += kKeepBlock) kp[i] = i < L ? (int32_t)i : -1;
+        return;
+    }
+    const int npre = (int)(L - w);
+    const int K = (int)(keep_eff - w);
+    const float *pl = pooled + bh * L_max;
+    if (K > 0) {
+        uint32_t thr;
+        int take_eq;
+        auto load = [&](int i) { return ordered_key(pl[i]); };
+        block_topk_threshold<kKeepBlock>(load, npre, K, hist, sh, thr, take_eq);
+        block_topk_emit<kKeepBlock>(load, npre, thr, take_eq, wave_tot,
+                                    [&](int o, int i) { kp[o] = i; });
+    }
+    for (int i = tid; i < w; i += kKeepBlock) kp[K + i] = npre + i;
+    for (int64_t i = keep_eff + tid; i < kept_stride; i += kKeepBlock) kp[i] = -1;
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+gather_kernel(int Hkv, int64_t L_max, EvictSeq seq, const int32_t *kept, int64_t kept_stride,
+              const T *k, const T *v, T *k_pool, T *v_pool, const int32_t *page_table, int P,
+              int max_pages, int64_t num_blocks) {
+    constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+    constexpr int RPB = 256 / CPR;
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int64_t L = seq.L[b];
+    const int64_t keep_eff = min<int64_t>(seq.keep[b], L);
+    const int64_t qrow = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
+    const int chunk = threadIdx.x % CPR;
+    if (qrow >= keep_eff) return;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int32_t t = kept[bh * kept_stride + qrow];
+    if (t < 0 || t >= L) return;
+    const int32_t blk = page_table[(int64_t)b * max_pages + qrow / P];
+    if (blk < 0 || blk >= num_blocks) return;
+    const int64_t src = (bh * L_max + t) * D;
+    const int64_t dst = (((int64_t)blk * Hkv + h) * P + qrow % P) * D;
+    ((uint4 *)(k_pool + dst))[chunk] = ((const uint4 *)(k + src))[chunk];
+    ((uint4 *)(v_pool + dst))[chunk] = ((const uint4 *)(v + src))[chunk];
+}
+
+template <typename T, int D>
+int launch_t(const rkv_gqa &g, int B, const EvictSeq &seq, int64_t L_max, int w, int pool_kernel,
+             float scale, const void *q_win, const void *k, const void *v,
+             const rkv_paged_cache &c, void *summaries, int32_t *kept_idx, int keep_stride,
+             float *pooled, int32_t *seq_lens_out, void *ws, hipStream_t s) {
+    const EvictWs l = evict_layout(g, B, L_max, w);
+    char *base = (char *)ws;
+    float *Z = (float *)(base + l.z), *TM = (float *)(base + l.tm);
+    float *M = (float *)(base + l.m), *ell = (float *)(base + l.ell);
+    double *PL = (double *)(base + l.pl);
+    float *A = (float *)(base + l.a);
+    float *pl = pooled ? pooled : (float *)(base + l.pooled);
+    int32_t *kept = kept_idx ? kept_idx : (int32_t *)(base + l.kept);
+    const int64_t kstride = kept_idx ? keep_stride : L_max;
+    int32_t *nold = (int32_t *)(base + l.nold), *nnew = (int32_t *)(base + l.nnew);
+    const int Hkv = g.n_kv_heads, G = g.group, R = l.R;
+    int64_t keep_rows = 0;
+    for (int b = 0; b < B; ++b) {
+        const int64_t ke = seq.keep[b] < seq.L[b] ? seq.keep[b] : seq.L[b];
+        if (ke > keep_rows) keep_rows = ke;
+    }
+    const int blocks_t = (int)((L_max + 255) / 256);
+
+    logits_kernel<T, D><<<dim3(l.ntiles, Hkv, B), kLogitsBlock, 0, s>>>(
+        Hkv, R, w, L_max, seq, (const T *)q_win, (const T *)k, scale, l.ntiles, Z, TM);
+    rowmax_kernel<<<dim3(Hkv, B), 256, 0, s>>>(Hkv, R, seq, l.ntiles, TM, M);
+    rowsum_kernel<<<dim3(l.nch, Hkv, B), 256, 0, s>>>(Hkv, R, w, L_max, seq, l.nch, Z, M, PL);
+    rowsum_final_kernel<<<dim3(Hkv, B), 256, 0, s>>>(Hkv, R, seq, l.nch, PL, ell);
+    colsum_kernel<<<dim3(blocks_t, Hkv, B), 256, 2 * R * sizeof(float), s>>>(
+        Hkv, G, w, L_max, seq, Z, M, ell, A);
+    maxpool_kernel<<<dim3(blocks_t, Hkv, B), 256, 0, s>>>(Hkv, w, L_max, seq, pool_kernel / 2, A, pl);
+    keep_kernel<<<dim3(Hkv, B), kKeepBlock, 0, s>>>(Hkv, w, L_max, seq, pl, kept, kstride, nold,
+                                                    nnew, seq_lens_out);
+    if (keep_rows > 0) {
+        constexpr int RPB = 256 / (D * (int)sizeof(T) / 16);
+        gather_kernel<T, D><<<dim3((int)((keep_rows + RPB - 1) / RPB), Hkv, B), 256, 0, s>>>(
+            Hkv, L_max, seq, kept, kstride, (const T *)k, (const T *)v, (T *)c.k_pool,
+            (T *)c.v_pool, c.page_table, c.page_size, c.max_pages, c.num_blocks);
+    }
+    int st = launch_status();
+    if (st != RKV_OK) return st;
+    if (summaries && keep_rows > 0)
+        return launch_append(g, sizeof(T) == 4 ? RKV_F32 : RKV_BF16, B, c, nold, nnew,
+                             (int)keep_rows, nullptr, nullptr, summaries, s);
+    return RKV_OK;
+}
+
+}  // namespace
+
+size_t evict_ws_bytes(const rkv_gqa &g, int B, int64_t L_max, int w) {
+    return evict_layout(g, B, L_max, w).total;
+}
+
+int launch_evict(const rkv_gqa &g, int dtype, int B, const EvictSeq &seq, int64_t L_max, int w,
+                 int pool_kernel, float scale, const void *q_win, const void *k, const void *v,
+                 const rkv_paged_cache &c, void *summaries, int32_t *kept_idx, int keep_stride,
+                 float *pooled, int32_t *seq_lens_out, void *ws, hipStream_t s) {
+    const int d = g.head_dim;
+    if (dtype == RKV_F32) {
+        if (d == 64) return launch_t<float, 64>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, s);
+        if (d == 128) return launch_t<float, 128>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, s);
+    } else {
+        if (d == 64) return launch_t<uint16_t, 64>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, s);
+        if (d == 128) return launch_t<uint16_t, 128>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, s);
+    }
+    return RKV_EUNSUPPORTED;
+}
+
+}  // namespace rkv

@@ -1,0 +1,222 @@
+// rkv_internal.h -- device helpers and internal launcher declarations shared
+// by the librkv translation units.  gfx950 only: 64-lane wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rkv.h"
+
+namespace rkv {
+
+constexpr int kWave = 64;
+
+// ---- element types ------------------------------------------------------
+// bf16 is carried as raw uint16_t bits; widening to fp32 is exact.
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+    static __device__ __forceinline__ float ld(const float *p, int64_t i) { return p[i]; }
+};
+template <>
+struct Elem<uint16_t> {
+    static __device__ __forceinline__ float ld(const uint16_t *p, int64_t i) {
+        return bf16_to_f32(p[i]);
+    }
+};
+
+// Unpack one 16-byte vector into fp32 lanes: 4 fp32 or 8 bf16 values.
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<float> {
+    static constexpr int N = 4;
+    static __device__ __forceinline__ void unpack(const uint4 &u, float *f) {
+        f[0] = __uint_as_float(u.x);
+        f[1] = __uint_as_float(u.y);
+        f[2] = __uint_as_float(u.z);
+        f[3] = __uint_as_float(u.w);
+    }
+};
+template <>
+struct Vec16<uint16_t> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ void unpack(const uint4 &u, float *f) {
+        f[0] = __uint_as_float(u.x << 16);
+        f[1] = __uint_as_float(u.x & 0xffff0000u);
+        f[2] = __uint_as_float(u.y << 16);
+        f[3] = __uint_as_float(u.y & 0xffff0000u);
+        f[4] = __uint_as_float(u.z << 16);
+        f[5] = __uint_as_float(u.z & 0xffff0000u);
+        f[6] = __uint_as_float(u.w << 16);
+        f[7] = __uint_as_float(u.w & 0xffff0000u);
+    }
+};
+
+// ---- ordering keys --------------------------------------------------------
+// Maps fp32 to uint32 so that unsigned order equals numeric order; -0 and +0
+// map to the same key.  Non-finite inputs are outside the contract.
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---- block-wide helpers ---------------------------------------------------
+// Exclusive prefix count of `flag` over the threads of the block, in thread
+// order.  `wave_tot` is LDS scratch of NW ints.  All threads must call it.
+template <int NW>
+__device__ __forceinline__ int block_excl_count(bool flag, int *wave_tot, int &total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const uint64_t b = __ballot(flag);
+    const uint64_t below = lane ? (b & (~0ull >> (64 - lane))) : 0ull;
+    const int in_wave = __popcll(below);
+    if (lane == 0) wave_tot[w] = __popcll(b);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int t = wave_tot[i];
+        off += (i < w) ? t : 0;
+        tot += t;
+    }
+    __syncthreads();
+    total = tot;
+    return off + in_wave;
+}
+
+// Radix select over the keys u[0..n): finds the K-th largest key `thr`
+// (1 <= K <= n) and how many keys equal to `thr` belong to the top K
+// (`take_eq`, the lowest-indexed ones).  `hist` is LDS of 256 uint32,
+// `sh` LDS of 2 ints.  All threads must call it.  `Load` maps i -> key.
+template <int BLOCK, typename Load>
+__device__ void block_topk_threshold(Load load, int n, int K, uint32_t *hist, int *sh,
+                                     uint32_t &thr, int &take_eq) {
+    uint32_t prefix = 0u, mask = 0u;
+    int remaining = K;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += BLOCK) hist[i] = 0u;
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += BLOCK) {
+            const uint32_t u = load(i);
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            const int lane = threadIdx.x;
+            // lane owns bins 255-4*lane .. 252-4*lane (descending order)
+            uint32_t c[4];
+            uint32_t mine = 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                c[q] = hist[255 - 4 * lane - q];
+                mine += c[q];
+            }
+            uint32_t incl = mine;
+#pragma unroll
+            for (int off = 1; off < kWave; off <<= 1) {
+                const uint32_t o = __shfl_up(incl, off, kWave);
+                if (lane >= off) incl += o;
+            }
+            const uint32_t excl = incl - mine;
+            if (excl < (uint32_t)remaining && (uint32_t)remaining <= incl) {
+                uint32_t cum = excl;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (cum + c[q] >= (uint32_t)remaining) {
+                        sh[0] = 255 - 4 * lane - q;
+                        sh[1] = (int)cum;
+                        break;
+                    }
+                    cum += c[q];
+                }
+            }
+        }
+        __syncthreads();
+        const uint32_t digit = (uint32_t)sh[0];
+        remaining -= sh[1];
+        prefix |= digit << shift;
+        mask |= 255u << shift;
+        __syncthreads();
+    }
+    thr = prefix;
+    take_eq = remaining;
+}
+
+// Writes, in ascending index order, the indices of the top-K keys found by
+// block_topk_threshold: emit(pos, i) for pos = 0..K-1.
+template <int BLOCK, typename Load, typename Emit>
+__device__ void block_topk_emit(Load load, int n, uint32_t thr, int take_eq, int *wave_tot,
+                                Emit emit) {
+    int eq_base = 0, sel_base = 0;
+    for (int i0 = 0; i0 < n; i0 += BLOCK) {
+        const int i = i0 + threadIdx.x;
+        const uint32_t u = i < n ? load(i) : 0u;
+        const bool eq = (i < n) && (u == thr);
+        int eq_tot;
+        const int eq_rank = eq_base + block_excl_count<BLOCK / kWave>(eq, wave_tot, eq_tot);
+        const bool sel = (i < n) && (u > thr || (eq && eq_rank < take_eq));
+        int sel_tot;
+        const int pos = sel_base + block_excl_count<BLOCK / kWave>(sel, wave_tot, sel_tot);
+        if (sel) emit(pos, i);
+        eq_base += eq_tot;
+        sel_base += sel_tot;
+    }
+}
+
+__device__ __forceinline__ float exp2_diff(float a, float b) {
+    // exp2(a - b) with exp2(-inf - x) = 0, also when both are -inf.
+    return (a == -INFINITY) ? 0.0f : exp2f(a - b);
+}
+
+// ---- launch helpers ------------------------------------------------------
+inline int launch_status() {
+    return hipGetLastError() == hipSuccess ? RKV_OK : RKV_EHIP;
+}
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+// ---- internal launchers (one translation unit each) -----------------------
+int launch_append(const rkv_gqa &g, int dtype, int B, const rkv_paged_cache &c,
+                  const int32_t *n_old, const int32_t *n_new, int max_new_rows,
+                  const void *k_src, const void *v_src, void *summaries, hipStream_t s);
+
+struct SelectPlan {
+    int chunk_pages;  // pages scored per block
+    int n_chunks;     // blocks per (sequence, KV head)
+};
+SelectPlan plan_select(const rkv_gqa &g, int B, int max_pages, int k2);
+size_t select_ws_bytes(const rkv_gqa &g, int B, int max_pages, int k2);
+int launch_select(const rkv_gqa &g, int dtype, int B, const void *q, const int32_t *seq_lens,
+                  int P, int max_pages, const void *summaries, int k1, int k2,
+                  int32_t *chan_idx, int32_t *page_idx, float *page_scores, void *ws,
+                  hipStream_t s);
+
+struct AttendPlan {
+    int pages_per_block;
+    int n_splits;
+};
+AttendPlan plan_attend(const rkv_gqa &g, int B, int P, int k2);
+size_t attend_ws_bytes(const rkv_gqa &g, int B, int P, int k2);
+int launch_attend(const rkv_gqa &g, int dtype, int B, const void *q,
+                  const rkv_paged_cache &c, const int32_t *seq_lens, const int32_t *page_idx,
+                  int k2, float scale, float *out, void *ws, hipStream_t s);
+
+struct EvictSeq {
+    int32_t L[RKV_MAX_EVICT_BATCH];
+    int32_t keep[RKV_MAX_EVICT_BATCH];
+};
+size_t evict_ws_bytes(const rkv_gqa &g, int B, int64_t L_max, int w);
+int launch_evict(const rkv_gqa &g, int dtype, int B, const EvictSeq &seq, int64_t L_max,
+                 int w, int pool_kernel, float scale, const void *q_win, const void *k,
+                 const void *v, const rkv_paged_cache &c, void *summaries,
+                 int32_t *kept_idx, int keep_stride, float *pooled, int32_t *seq_lens_out,
+                 void *ws, hipStream_t s);
+
+}  // namespace rkv

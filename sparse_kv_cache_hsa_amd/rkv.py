@@ -1,0 +1,302 @@
+"""Thin ctypes binding of librkv (the C ABI in include/rkv.h).
+
+Argument marshalling only: every step of the decode path runs in librkv's
+HIP kernels.  Tensors are torch CUDA tensors (PyTorch supplies device memory
+and the current stream); dtypes map float32 -> RKV_F32, bfloat16 -> RKV_BF16.
+The library is loaded on first use and must have been built from the
+sources next to it (``sparse_kv_cache_hsa_amd.build``); a missing or stale
+build raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+
+import torch
+
+from . import build as _build
+
+RKV_OK = 0
+RKV_EINVAL = -1
+RKV_EWORKSPACE = -2
+RKV_ECAPACITY = -3
+RKV_EUNSUPPORTED = -4
+RKV_EHIP = -5
+RKV_F32 = 0
+RKV_BF16 = 1
+RKV_MAX_K2 = 1024
+RKV_MAX_EVICT_BATCH = 128
+
+EXPORTED = (
+    "rkv_status_string", "rkv_build_id", "rkv_split_ratio",
+    "rkv_prefill_evict_workspace_bytes", "rkv_prefill_evict", "rkv_append_summaries",
+    "rkv_hsa_workspace_bytes", "rkv_hsa_select", "rkv_hsa_attend", "rkv_hsa_decode",
+)
+
+
+class RkvError(RuntimeError):
+    def __init__(self, where: str, status: int, text: str):
+        super().__init__(f"{where}: status {status} ({text})")
+        self.status = status
+
+
+class rkv_gqa(ctypes.Structure):
+    _fields_ = [("n_kv_heads", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32)]
+
+
+class rkv_paged_cache(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("num_blocks", ctypes.c_int64),
+                ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
+
+
+_LOCK = threading.Lock()
+_LIB = None
+
+
+def load_library(path: str | None = None, check_build_id: bool = True):
+    """Loads librkv.so (once).  Raises if it is missing or stale."""
+    global _LIB
+    with _LOCK:
+        if _LIB is not None:
+            return _LIB
+        path = path or _build.LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(path)
+        i32, i64, f32, f64, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                      ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t)
+        P = ctypes.POINTER
+        G, C = P(rkv_gqa), P(rkv_paged_cache)
+        lib.rkv_status_string.argtypes = [ctypes.c_int]
+        lib.rkv_status_string.restype = ctypes.c_char_p
+        lib.rkv_build_id.argtypes = []
+        lib.rkv_build_id.restype = ctypes.c_char_p
+        lib.rkv_split_ratio.argtypes = [f64, i64, i64, P(f64), P(f64), P(f64), P(i64)]
+        lib.rkv_split_ratio.restype = ctypes.c_int
+        lib.rkv_prefill_evict_workspace_bytes.argtypes = [G, i32, i64, i32]
+        lib.rkv_prefill_evict_workspace_bytes.restype = sz
+        lib.rkv_prefill_evict.argtypes = [G, i32, i32, P(i32), P(i32), i64, i32, i32, f32, vp,
+                                          vp, vp, C, vp, vp, i32, vp, vp, vp, sz, vp]
+        lib.rkv_prefill_evict.restype = ctypes.c_int
+        lib.rkv_append_summaries.argtypes = [G, i32, i32, C, vp, vp, i32, vp, vp, vp, vp]
+        lib.rkv_append_summaries.restype = ctypes.c_int
+        lib.rkv_hsa_workspace_bytes.argtypes = [G, i32, i32, i32, i32, i32]
+        lib.rkv_hsa_workspace_bytes.restype = sz
+        lib.rkv_hsa_select.argtypes = [G, i32, i32, vp, vp, i32, i32, vp, i32, i32, vp, vp, vp,
+                                       vp, sz, vp]
+        lib.rkv_hsa_select.restype = ctypes.c_int
+        lib.rkv_hsa_attend.argtypes = [G, i32, i32, vp, C, vp, vp, i32, f32, vp, vp, sz, vp]
+        lib.rkv_hsa_attend.restype = ctypes.c_int
+        lib.rkv_hsa_decode.argtypes = [G, i32, i32, vp, C, vp, vp, i32, i32, f32, vp, vp, vp,
+                                       vp, vp, sz, vp]
+        lib.rkv_hsa_decode.restype = ctypes.c_int
+        if check_build_id:
+            built = lib.rkv_build_id().decode()
+            want = _build.source_hash()
+            if built != want:
+                raise RuntimeError(f"{path} was built from other sources (build id {built}, "
+                                   f"sources {want}); run __graft_entry__.build() again")
+        _LIB = lib
+        return lib
+
+
+def _check(where: str, status: int) -> None:
+    if status != RKV_OK:
+        raise RkvError(where, status, load_library().rkv_status_string(status).decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RKV_F32
+    if t.dtype == torch.bfloat16:
+        return RKV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor | None, name: str, dtype=None, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def gqa(n_kv_heads: int, group: int, head_dim: int) -> rkv_gqa:
+    return rkv_gqa(int(n_kv_heads), int(group), int(head_dim))
+
+
+@dataclass
+class PagedCache:
+    """A paged KV cache as librkv sees it (tensors are caller-owned)."""
+    k_pool: torch.Tensor      # [num_blocks, Hkv, P, d]
+    v_pool: torch.Tensor      # [num_blocks, Hkv, P, d]
+    page_table: torch.Tensor  # [B, max_pages] int32
+
+    @property
+    def page_size(self) -> int:
+        return int(self.k_pool.shape[2])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.page_table.shape[1])
+
+    def c_struct(self) -> rkv_paged_cache:
+        _need(self.k_pool, "k_pool")
+        _need(self.v_pool, "v_pool", self.k_pool.dtype)
+        _need(self.page_table, "page_table", torch.int32)
+        return rkv_paged_cache(self.k_pool.data_ptr(), self.v_pool.data_ptr(),
+                               self.page_table.data_ptr(), int(self.k_pool.shape[0]),
+                               self.page_size, self.max_pages)
+
+    def row_slice(self, b0: int, b1: int) -> "PagedCache":
+        """The same pools with the page-table rows of sequences [b0, b1)."""
+        return PagedCache(self.k_pool, self.v_pool, self.page_table[b0:b1])
+
+
+# ---- entry points (same names as the C ABI) ---------------------------------
+
+def rkv_split_ratio(c: float, L: int, w: int = 0):
+    """Returns (r, c_evict, c_hsa, keep)."""
+    r, ce, ch = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    keep = ctypes.c_int64()
+    _check("rkv_split_ratio", load_library().rkv_split_ratio(
+        float(c), int(L), int(w), ctypes.byref(r), ctypes.byref(ce), ctypes.byref(ch),
+        ctypes.byref(keep)))
+    return r.value, ce.value, ch.value, keep.value
+
+
+def rkv_prefill_evict_workspace_bytes(g: rkv_gqa, B: int, L_max: int, w: int) -> int:
+    return int(load_library().rkv_prefill_evict_workspace_bytes(ctypes.byref(g), B, L_max, w))
+
+
+def rkv_prefill_evict(g: rkv_gqa, prompt_lens, keep, q_win: torch.Tensor, k: torch.Tensor,
+                      v: torch.Tensor, w: int, pool_kernel: int, scale: float,
+                      cache: PagedCache, summaries: torch.Tensor | None = None,
+                      kept_idx: torch.Tensor | None = None,
+                      pooled_scores: torch.Tensor | None = None,
+                      seq_lens_out: torch.Tensor | None = None,
+                      ws: torch.Tensor | None = None) -> None:
+    """SnapKV++ eviction.  prompt_lens/keep: host sequences of ints (length B);
+    q_win [B, Hq, w, d]; k, v [B, Hkv, L_max, d]."""
+    _need(k, "k")
+    _need(v, "v", k.dtype)
+    _need(q_win, "q_win", k.dtype)
+    _need(summaries, "summaries", k.dtype, optional=True)
+    _need(kept_idx, "kept_idx", torch.int32, optional=True)
+    _need(pooled_scores, "pooled_scores", torch.float32, optional=True)
+    _need(seq_lens_out, "seq_lens_out", torch.int32, optional=True)
+    B, L_max = int(k.shape[0]), int(k.shape[2])
+    lens = (ctypes.c_int32 * B)(*[int(x) for x in prompt_lens])
+    keeps = (ctypes.c_int32 * B)(*[int(x) for x in keep])
+    if ws is None:
+        ws = torch.empty(rkv_prefill_evict_workspace_bytes(g, B, L_max, w), dtype=torch.uint8,
+                         device=k.device)
+    _need(ws, "ws")
+    cs = cache.c_struct()
+    stride = int(kept_idx.shape[-1]) if kept_idx is not None else 0
+    _check("rkv_prefill_evict", load_library().rkv_prefill_evict(
+        ctypes.byref(g), _dtype_code(k), B, lens, keeps, L_max, int(w), int(pool_kernel),
+        float(scale), q_win.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(cs),
+        _ptr(summaries), _ptr(kept_idx), stride, _ptr(pooled_scores), _ptr(seq_lens_out),
+        ws.data_ptr(), ws.numel(), _stream()))
+
+
+def rkv_append_summaries(g: rkv_gqa, cache: PagedCache, n_old: torch.Tensor,
+                         n_new: torch.Tensor, max_new_rows: int, summaries: torch.Tensor,
+                         k_src: torch.Tensor | None = None,
+                         v_src: torch.Tensor | None = None) -> None:
+    """Fold rows [n_old, n_new) into the page summaries, first copying them
+    from k_src/v_src [B, Hkv, max_new_rows, d] into the cache when given."""
+    _need(n_old, "n_old", torch.int32)
+    _need(n_new, "n_new", torch.int32)
+    _need(summaries, "summaries", cache.k_pool.dtype)
+    _need(k_src, "k_src", cache.k_pool.dtype, optional=True)
+    _need(v_src, "v_src", cache.k_pool.dtype, optional=True)
+    cs = cache.c_struct()
+    _check("rkv_append_summaries", load_library().rkv_append_summaries(
+        ctypes.byref(g), _dtype_code(summaries), int(n_old.shape[0]), ctypes.byref(cs),
+        n_old.data_ptr(), n_new.data_ptr(), int(max_new_rows), _ptr(k_src), _ptr(v_src),
+        summaries.data_ptr(), _stream()))
+
+
+def rkv_hsa_workspace_bytes(g: rkv_gqa, B: int, page_size: int, max_pages: int, k1: int,
+                            k2: int) -> int:
+    return int(load_library().rkv_hsa_workspace_bytes(ctypes.byref(g), B, page_size,
+                                                      max_pages, k1, k2))
+
+
+def hsa_workspace(g: rkv_gqa, B: int, page_size: int, max_pages: int, k1: int, k2: int,
+                  device) -> torch.Tensor:
+    return torch.zeros(rkv_hsa_workspace_bytes(g, B, page_size, max_pages, k1, k2),
+                       dtype=torch.uint8, device=device)
+
+
+def rkv_hsa_select(g: rkv_gqa, q: torch.Tensor, seq_lens: torch.Tensor, page_size: int,
+                   summaries: torch.Tensor, k1: int, k2: int, page_idx: torch.Tensor,
+                   ws: torch.Tensor, chan_idx: torch.Tensor | None = None,
+                   page_scores: torch.Tensor | None = None) -> None:
+    _need(q, "q")
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(summaries, "summaries", q.dtype)
+    _need(page_idx, "page_idx", torch.int32)
+    _need(chan_idx, "chan_idx", torch.int32, optional=True)
+    _need(page_scores, "page_scores", torch.float32, optional=True)
+    _need(ws, "ws")
+    max_pages = int(summaries.shape[-1])
+    _check("rkv_hsa_select", load_library().rkv_hsa_select(
+        ctypes.byref(g), _dtype_code(q), int(q.shape[0]), q.data_ptr(), seq_lens.data_ptr(),
+        int(page_size), max_pages, summaries.data_ptr(), int(k1), int(k2), _ptr(chan_idx),
+        page_idx.data_ptr(), _ptr(page_scores), ws.data_ptr(), ws.numel(), _stream()))
+
+
+def rkv_hsa_attend(g: rkv_gqa, q: torch.Tensor, cache: PagedCache, seq_lens: torch.Tensor,
+                   page_idx: torch.Tensor, k2: int, scale: float, out: torch.Tensor,
+                   ws: torch.Tensor) -> None:
+    _need(q, "q", cache.k_pool.dtype)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(page_idx, "page_idx", torch.int32)
+    _need(out, "out", torch.float32)
+    _need(ws, "ws")
+    cs = cache.c_struct()
+    _check("rkv_hsa_attend", load_library().rkv_hsa_attend(
+        ctypes.byref(g), _dtype_code(q), int(q.shape[0]), q.data_ptr(), ctypes.byref(cs),
+        seq_lens.data_ptr(), page_idx.data_ptr(), int(k2), float(scale), out.data_ptr(),
+        ws.data_ptr(), ws.numel(), _stream()))
+
+
+def rkv_hsa_decode(g: rkv_gqa, q: torch.Tensor, cache: PagedCache, seq_lens: torch.Tensor,
+                   summaries: torch.Tensor, k1: int, k2: int, scale: float, out: torch.Tensor,
+                   ws: torch.Tensor, chan_idx: torch.Tensor | None = None,
+                   page_idx: torch.Tensor | None = None,
+                   page_scores: torch.Tensor | None = None) -> None:
+    _need(q, "q", cache.k_pool.dtype)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(summaries, "summaries", q.dtype)
+    _need(out, "out", torch.float32)
+    _need(chan_idx, "chan_idx", torch.int32, optional=True)
+    _need(page_idx, "page_idx", torch.int32, optional=True)
+    _need(page_scores, "page_scores", torch.float32, optional=True)
+    _need(ws, "ws")
+    cs = cache.c_struct()
+    _check("rkv_hsa_decode", load_library().rkv_hsa_decode(
+        ctypes.byref(g), _dtype_code(q), int(q.shape[0]), q.data_ptr(), ctypes.byref(cs),
+        seq_lens.data_ptr(), summaries.data_ptr(), int(k1), int(k2), float(scale),
+        out.data_ptr(), _ptr(chan_idx), _ptr(page_idx), _ptr(page_scores), ws.data_ptr(),
+        ws.numel(), _stream()))

@@ -1,0 +1,113 @@
+"""Host-side checks of librkv without a GPU: it loads, exports every function
+include/rkv.h declares, was built from the current sources, computes the
+adaptive split like the oracle, and rejects bad arguments before touching
+the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rkv_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(rkv_lib):
+    lib = rkv_lib.load_library()
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(rkv_lib.EXPORTED)
+
+
+def test_build_id_matches_sources(rkv_lib):
+    from sparse_kv_cache_hsa_amd import build
+    assert rkv_lib.load_library().rkv_build_id().decode() == build.source_hash()
+
+
+@pytest.mark.parametrize("c", [1.0, 1.25, 2.0, 7.0, 16.0, 31.99, 64.0, 428.0, 1024.0, 3e5])
+@pytest.mark.parametrize("L,w", [(0, 0), (1, 0), (32768, 32), (109568, 32), (16384, 32), (10, 32)])
+def test_split_matches_oracle_bitwise(rkv_lib, c, L, w):
+    assert rkv_lib.rkv_split_ratio(c, L, w) == oracle.split_ratio(c, L, w)
+
+
+def test_split_rejects_bad_ratio(rkv_lib):
+    for c in (0.99, float("nan"), float("inf"), -1.0):
+        with pytest.raises(rkv_lib.RkvError) as e:
+            rkv_lib.rkv_split_ratio(c, 10, 0)
+        assert e.value.status == rkv_lib.RKV_EINVAL
+
+
+def _call_decode(lib, g, dtype=0, B=1, P=16, max_pages=8, k1=8, k2=4, scale=0.125,
+                 ws_bytes=1 << 20, null_q=False, null_out=False):
+    fake = 0x10000  # never dereferenced: every case below fails a host check
+    cache = lib.rkv_paged_cache(fake, fake, fake, 64, P, max_pages)
+    return lib.load_library().rkv_hsa_decode(
+        ctypes.byref(g) if g is not None else None, dtype, B, None if null_q else fake,
+        ctypes.byref(cache), fake, fake, k1, k2, scale, None if null_out else fake,
+        None, None, None, fake, ws_bytes, None)
+
+
+def test_decode_argument_checks(rkv_lib):
+    L = rkv_lib
+    g = L.gqa(8, 4, 128)
+    assert _call_decode(L, None) == L.RKV_EINVAL
+    assert _call_decode(L, L.gqa(8, 3, 128)) == L.RKV_EUNSUPPORTED
+    assert _call_decode(L, L.gqa(8, 4, 96)) == L.RKV_EUNSUPPORTED
+    assert _call_decode(L, g, dtype=7) == L.RKV_EUNSUPPORTED
+    assert _call_decode(L, g, B=0) == L.RKV_EINVAL
+    assert _call_decode(L, g, k1=0) == L.RKV_EINVAL
+    assert _call_decode(L, g, k1=129) == L.RKV_EINVAL
+    assert _call_decode(L, g, k2=0) == L.RKV_EINVAL
+    assert _call_decode(L, g, k2=L.RKV_MAX_K2 + 1) == L.RKV_EINVAL
+    assert _call_decode(L, g, P=0) == L.RKV_EINVAL
+    assert _call_decode(L, g, P=300) == L.RKV_EUNSUPPORTED
+    assert _call_decode(L, g, scale=0.0) == L.RKV_EINVAL
+    assert _call_decode(L, g, scale=float("nan")) == L.RKV_EINVAL
+    assert _call_decode(L, g, null_q=True) == L.RKV_EINVAL
+    assert _call_decode(L, g, null_out=True) == L.RKV_EINVAL
+    assert _call_decode(L, g, ws_bytes=16) == L.RKV_EWORKSPACE
+
+
+def test_workspace_sizes(rkv_lib):
+    L = rkv_lib
+    g = L.gqa(8, 4, 128)
+    a = L.rkv_hsa_workspace_bytes(g, 1, 16, 256, 32, 32)
+    b = L.rkv_hsa_workspace_bytes(g, 32, 16, 400, 32, 64)
+    assert 0 < a <= b
+    e1 = L.rkv_prefill_evict_workspace_bytes(g, 1, 32768, 32)
+    # logits for 128 window rows over 32K keys dominate: 4 B each
+    assert e1 >= 8 * 32768 * 128 * 4
+    assert L.rkv_prefill_evict_workspace_bytes(L.gqa(8, 3, 128), 1, 100, 8) == 0
+
+
+def test_evict_argument_checks(rkv_lib):
+    L = rkv_lib
+    lib = L.load_library()
+    g = L.gqa(2, 2, 64)
+    fake = 0x10000
+    cache = L.rkv_paged_cache(fake, fake, fake, 64, 16, 4)
+
+    def call(lens, keeps, w=8, pool=7, L_max=100, stride=0, ws=1 << 30):
+        B = len(lens)
+        return lib.rkv_prefill_evict(
+            ctypes.byref(g), 0, B, (ctypes.c_int32 * B)(*lens), (ctypes.c_int32 * B)(*keeps),
+            L_max, w, pool, 0.125, fake, fake, fake, ctypes.byref(cache), None,
+            fake if stride else None, stride, None, None, fake, ws, None)
+
+    assert call([50], [20], pool=4) == L.RKV_EINVAL          # even pooling kernel
+    assert call([50], [5]) == L.RKV_EINVAL                   # keep below window
+    assert call([150], [20]) == L.RKV_EINVAL                 # prompt longer than L_max
+    assert call([100], [80]) == L.RKV_ECAPACITY              # 80 rows > 4 pages x 16
+    assert call([50], [20], stride=10) == L.RKV_EINVAL       # kept_idx row too short
+    assert call([50], [20], ws=100) == L.RKV_EWORKSPACE
+    assert call([50] * 200, [20] * 200) == L.RKV_EUNSUPPORTED  # batch above the limit

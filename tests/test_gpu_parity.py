@@ -1,0 +1,247 @@
+"""GPU parity of every librkv entry point against the CPU oracle on small and
+ragged shapes: page summaries (bit-exact), HSA channel/page selection and page
+scores (bit-exact), attention outputs (within 1e-3), SnapKV++ kept sets (gap
+rule) and the compacted cache.  Inputs are seeded; both sides read the same
+bytes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_kv_cache_hsa_amd import synth, workloads
+
+from _helpers import (OUT_ATOL, bits, check_kept, fill_cache, gpu_summaries, lib, make_cache,
+                      max_abs_err, n_pages, oracle_summaries, scale_for)
+
+pytestmark = pytest.mark.gpu
+F32, BF16 = torch.float32, torch.bfloat16
+
+
+def rand(shape, seed, dtype, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(dtype)
+
+
+# (dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages)
+DECODE_CASES = [
+    (F32, 1, 2, 4, 64, 16, 16, 16, [2048], 136),
+    (BF16, 3, 2, 4, 128, 16, 32, 8, [1000, 17, 1], 64),
+    (BF16, 2, 1, 8, 128, 1, 32, 64, [300, 129], 512),
+    (F32, 2, 3, 1, 64, 7, 64, 5, [100, 0], 32),
+    (BF16, 1, 4, 2, 64, 32, 8, 200, [1500], 64),
+    (BF16, 2, 8, 4, 128, 16, 32, 64, [5000, 4100], 400),
+    (BF16, 1, 2, 4, 128, 8, 16, 32, [1359], 200),
+    (F32, 1, 2, 2, 128, 32, 128, 1024, [8000], 260),
+    (BF16, 1, 1, 4, 128, 4, 32, 50, [20000], 5000),
+    (F32, 4, 2, 8, 64, 3, 5, 7, [1, 2, 3, 250], 100),
+]
+
+
+def run_decode_case(case, seed, q_override=None, k_override=None):
+    rkv = lib()
+    dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages = case
+    Lmax = max(max(lens), 1)
+    K = k_override if k_override is not None else rand((B, Hkv, Lmax, d), seed, dtype, 1.5)
+    V = rand((B, Hkv, Lmax, d), seed + 1, dtype)
+    q = q_override if q_override is not None else rand((B, Hkv * G, d), seed + 2, dtype)
+    g = rkv.gqa(Hkv, G, d)
+    pages = [min(max_pages, n_pages(n, P) + 1) for n in lens]
+    cache, summ = make_cache(Hkv, d, P, max_pages, pages, dtype, seed)
+    Kd, Vd, qd = K.cuda(), V.cuda(), q.cuda()
+    fill_cache(g, cache, summ, Kd, Vd, lens)
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = torch.full((B, Hkv * G, d), float("nan"), device="cuda")
+    chan = torch.full((B, Hkv, k1), -7, dtype=torch.int32, device="cuda")
+    pidx = torch.full((B, Hkv, k2), -7, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((B, Hkv, max_pages), dtype=torch.float32, device="cuda")
+    ws = rkv.hsa_workspace(g, B, P, max_pages, k1, k2, "cuda")
+    scale = scale_for(d)
+    rkv.rkv_hsa_decode(g, qd, cache, seq, summ, k1, k2, scale, out, ws, chan_idx=chan,
+                       page_idx=pidx, page_scores=scores)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for b in range(B):
+        n = lens[b]
+        NP = n_pages(n, P)
+        for h in range(Hkv):
+            kb, vb = bits(K[b, h, :max(n, 1)]), bits(V[b, h, :max(n, 1)])
+            smax, smin = oracle_summaries(bits(K[b, h, :n]), P, NP, d)
+            gmax, gmin = gpu_summaries(summ, b, h, NP)
+            if NP:
+                np.testing.assert_array_equal(gmax, smax)
+                np.testing.assert_array_equal(gmin, smin)
+            c_o, p_o, S_o, out_o = oracle.hsa_group(bits(q[b, h * G:(h + 1) * G]), kb, vb, smax,
+                                                    smin, n, P, k1, k2, scale)
+            np.testing.assert_array_equal(chan[b, h].cpu().numpy(), c_o)
+            np.testing.assert_array_equal(pidx[b, h].cpu().numpy(), p_o)
+            np.testing.assert_array_equal(scores[b, h, :NP].cpu().numpy().view(np.uint32),
+                                          S_o.view(np.uint32))
+            err = max_abs_err(out[b, h * G:(h + 1) * G], out_o)
+            assert err <= OUT_ATOL, (b, h, err)
+            worst = max(worst, err)
+    return worst, out
+
+
+@pytest.mark.parametrize("ci", range(len(DECODE_CASES)))
+def test_decode_matches_oracle(ci):
+    run_decode_case(DECODE_CASES[ci], 1000 + ci)
+
+
+def test_decode_ties_zero_query_and_identical_keys():
+    case = (BF16, 2, 2, 4, 128, 16, 32, 8, [700, 333], 64)
+    q = torch.zeros((2, 8, 128), dtype=BF16)
+    run_decode_case(case, 7, q_override=q)
+    K = rand((2, 2, 1, 128), 8, BF16).expand(2, 2, 700, 128).contiguous()
+    run_decode_case(case, 9, k_override=K)
+
+
+def test_decode_is_deterministic():
+    case = DECODE_CASES[5]
+    _, a = run_decode_case(case, 42)
+    _, b = run_decode_case(case, 42)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_append_in_chunks_matches_rebuild(dtype):
+    rkv = lib()
+    B, Hkv, d, P, max_pages = 3, 2, 64, 16, 40
+    g = rkv.gqa(Hkv, 2, d)
+    lens = [600, 37, 1]
+    K = rand((B, Hkv, 600, d), 5, dtype)
+    V = rand((B, Hkv, 600, d), 6, dtype)
+    cache, summ = make_cache(Hkv, d, P, max_pages, [max_pages] * B, dtype, 3)
+    Kd, Vd = K.cuda(), V.cuda()
+    done = [0] * B
+    for step, chunk in enumerate([1, 15, 16, 100, 3, 1000]):
+        new = [min(lens[b], done[b] + chunk) for b in range(B)]
+        mx = max(max(nn - o for nn, o in zip(new, done)), 1)
+        src_k = torch.zeros((B, Hkv, mx, d), dtype=dtype, device="cuda")
+        src_v = torch.zeros_like(src_k)
+        for b in range(B):
+            src_k[b, :, :new[b] - done[b]] = Kd[b, :, done[b]:new[b]]
+            src_v[b, :, :new[b] - done[b]] = Vd[b, :, done[b]:new[b]]
+        rkv.rkv_append_summaries(g, cache, torch.tensor(done, dtype=torch.int32, device="cuda"),
+                                 torch.tensor(new, dtype=torch.int32, device="cuda"), mx, summ,
+                                 k_src=src_k, v_src=src_v)
+        done = new
+    torch.cuda.synchronize()
+    table = cache.page_table.cpu()
+    for b in range(B):
+        NP = n_pages(lens[b], P)
+        for h in range(Hkv):
+            smax, smin = oracle.summaries_rebuild(bits(K[b, h, :lens[b]]), P)
+            gmax, gmin = gpu_summaries(summ, b, h, NP)
+            np.testing.assert_array_equal(gmax, smax)
+            np.testing.assert_array_equal(gmin, smin)
+            for p in range(NP):  # rows landed in the right blocks
+                rows = cache.k_pool[table[b, p], h, :min(P, lens[b] - p * P)].cpu()
+                assert torch.equal(rows, K[b, h, p * P:p * P + rows.shape[0]])
+    # rebuild from the pool (no copy-in) gives the same bits
+    summ2 = torch.zeros_like(summ)
+    rkv.rkv_append_summaries(g, cache, torch.zeros(B, dtype=torch.int32, device="cuda"),
+                             torch.tensor(lens, dtype=torch.int32, device="cuda"), 600, summ2)
+    torch.cuda.synchronize()
+    assert torch.equal(summ.view(torch.int16 if dtype == BF16 else torch.int32),
+                       summ2.view(torch.int16 if dtype == BF16 else torch.int32))
+
+
+def test_tiny_workload_decode_loop():
+    """The tiny fp32 workload end to end: 2,048 cached rows, 32 decode steps,
+    each appending its token through the library before HSA."""
+    rkv = lib()
+    wl = workloads.TINY
+    B, Hkv, G, d, P = wl.batch, wl.n_kv_heads, wl.group, wl.head_dim, wl.page_size
+    n0 = wl.cache_len
+    cap = n0 + wl.decode_steps
+    max_pages = n_pages(cap, P)
+    g = rkv.gqa(Hkv, G, d)
+    k0, v0 = wl.prompt_kv(0, 0, n0)
+    cache, summ = make_cache(Hkv, d, P, max_pages, [max_pages], wl.dtype, 1)
+    fill_cache(g, cache, summ, k0[None].cuda(), v0[None].cuda(), [n0])
+    K = np.zeros((cap, d), np.float32)
+    V = np.zeros((cap, d), np.float32)
+    Ko = [K.copy() for _ in range(Hkv)]
+    Vo = [V.copy() for _ in range(Hkv)]
+    smax = [np.zeros((max_pages, d), np.float32) for _ in range(Hkv)]
+    smin = [np.zeros((max_pages, d), np.float32) for _ in range(Hkv)]
+    for h in range(Hkv):
+        Ko[h][:n0], Vo[h][:n0] = k0[h].numpy(), v0[h].numpy()
+        oracle.summaries_append(Ko[h], 0, n0, P, smax[h], smin[h])
+    ws = rkv.hsa_workspace(g, B, P, max_pages, wl.k1, wl.k2, "cuda")
+    out = torch.zeros((B, Hkv * G, d), device="cuda")
+    pidx = torch.zeros((B, Hkv, wl.k2), dtype=torch.int32, device="cuda")
+    chan = torch.zeros((B, Hkv, wl.k1), dtype=torch.int32, device="cuda")
+    scale = scale_for(d)
+    n = n0
+    for step in range(wl.decode_steps):
+        kt, vt, qt = wl.decode_tokens(0, step, torch.tensor([n]))
+        rkv.rkv_append_summaries(g, cache, torch.tensor([n], dtype=torch.int32, device="cuda"),
+                                 torch.tensor([n + 1], dtype=torch.int32, device="cuda"), 1, summ,
+                                 k_src=kt[:, :, None].cuda(), v_src=vt[:, :, None].cuda())
+        seq = torch.tensor([n + 1], dtype=torch.int32, device="cuda")
+        rkv.rkv_hsa_decode(g, qt.cuda(), cache, seq, summ, wl.k1, wl.k2, scale, out, ws,
+                           chan_idx=chan, page_idx=pidx)
+        torch.cuda.synchronize()
+        for h in range(Hkv):
+            Ko[h][n], Vo[h][n] = kt[0, h].numpy(), vt[0, h].numpy()
+            oracle.summaries_append(Ko[h], n, n + 1, P, smax[h], smin[h])
+            c_o, p_o, _, out_o = oracle.hsa_group(qt[0, h * G:(h + 1) * G].numpy(), Ko[h], Vo[h],
+                                                  smax[h], smin[h], n + 1, P, wl.k1, wl.k2, scale)
+            np.testing.assert_array_equal(chan[0, h].cpu().numpy(), c_o)
+            np.testing.assert_array_equal(pidx[0, h].cpu().numpy(), p_o)
+            assert max_abs_err(out[0, h * G:(h + 1) * G], out_o) <= OUT_ATOL
+        n += 1
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("pool", [1, 7, 63])
+def test_prefill_evict_matches_oracle(dtype, pool):
+    rkv = lib()
+    B, Hkv, G, d, w, P = 3, 2, 4, 64, 16, 16
+    lens = [500, 1700, 3000]
+    keeps = [100, 300, 3000 if pool == 1 else 500]   # one case keeps everything
+    L_max = max(lens)
+    g = rkv.gqa(Hkv, G, d)
+    K = rand((B, Hkv, L_max, d), 21 + pool, dtype, 1.5)
+    V = rand((B, Hkv, L_max, d), 22 + pool, dtype)
+    Q = rand((B, Hkv * G, w, d), 23 + pool, dtype)
+    max_pages = n_pages(max(keeps), P) + 2
+    cache, summ = make_cache(Hkv, d, P, max_pages, [max_pages] * B, dtype, 4)
+    keep_eff = [min(k, L) for k, L in zip(keeps, lens)]
+    kept = torch.full((B, Hkv, max(keep_eff)), -7, dtype=torch.int32, device="cuda")
+    pooled = torch.zeros((B, Hkv, L_max), dtype=torch.float32, device="cuda")
+    seq_out = torch.zeros(B, dtype=torch.int32, device="cuda")
+    scale = scale_for(d)
+    rkv.rkv_prefill_evict(g, lens, keeps, Q.cuda(), K.cuda(), V.cuda(), w, pool, scale, cache,
+                          summaries=summ, kept_idx=kept, pooled_scores=pooled,
+                          seq_lens_out=seq_out)
+    torch.cuda.synchronize()
+    assert seq_out.cpu().tolist() == keep_eff
+    table = cache.page_table.cpu()
+    swaps = 0
+    for b in range(B):
+        L, ke = lens[b], keep_eff[b]
+        for h in range(Hkv):
+            kb = bits(K[b, h, :L])
+            k_o, A_o, pl_o = oracle.snapkv_group(bits(Q[b, h * G:(h + 1) * G]), kb, pool, keeps[b],
+                                                 scale)
+            gk = kept[b, h].cpu().numpy()
+            assert np.all(gk[ke:] == -1)
+            if keeps[b] < L:
+                gp = pooled[b, h, :L - w].cpu().numpy()
+                np.testing.assert_allclose(gp, pl_o, rtol=1e-5, atol=0)
+                swaps += check_kept(gk[:ke], k_o, pl_o, w)
+            else:
+                np.testing.assert_array_equal(gk[:ke], k_o)
+            # the compacted cache holds the kept rows in order
+            rows_k = torch.stack([cache.k_pool[table[b, r // P], h, r % P] for r in range(ke)])
+            rows_v = torch.stack([cache.v_pool[table[b, r // P], h, r % P] for r in range(ke)])
+            idx = torch.from_numpy(gk[:ke].astype(np.int64))
+            assert torch.equal(rows_k.cpu(), K[b, h, idx])
+            assert torch.equal(rows_v.cpu(), V[b, h, idx])
+            smax, smin = oracle.summaries_rebuild(bits(K[b, h, idx]), P)
+            gmax, gmin = gpu_summaries(summ, b, h, n_pages(ke, P))
+            np.testing.assert_array_equal(gmax, smax)
+            np.testing.assert_array_equal(gmin, smin)
+    print(f"near-tie boundary swaps: {swaps}")
