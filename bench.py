@@ -1,0 +1,256 @@
+"""Decode throughput of the RocketKV path on one MI355X.
+
+A step is one decode step of the whole model: for every layer, append the new
+token's K/V (and fold it into the page summaries), then Hybrid Sparse
+Attention (channel ranking, page bound scores, page top-k2, attention over
+the selected pages).  Caches are first pruned by SnapKV++ (timed separately,
+reported as stage1).  Steps are HIP-graph replays of the captured launches;
+inputs are resident in HBM before the timed region starts.
+
+Default workload: all 32 Llama3.1-8B layers, batch 32, contexts 16K-32K,
+budget 1,024 tokens per sequence.  Prints one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "HSA decode steps/s + attended tokens/s, achieved HBM GB/s vs peak, 32K ctx"
+DEFAULT_WORKLOAD = "llama8b-32layer-b32-ctx16k-32k"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attended_rows(sess, layer_page_idx, rows_now):
+    """Valid rows in the selected pages, per (sequence, KV head), summed."""
+    import torch
+    P = sess.P
+    pidx = layer_page_idx.cpu().to(torch.int64)            # [B, Hkv, k2]
+    n = torch.tensor(rows_now, dtype=torch.int64)[:, None, None]
+    valid = (pidx >= 0)
+    rows = torch.clamp(n - pidx * P, min=0, max=P) * valid
+    return int(rows.sum())
+
+
+def step_bytes(sess, rows_now, per_head_rows):
+    """Algorithmic HBM bytes of one decode step over every layer.
+    per_head_rows: attended rows summed over (sequence, KV head) of a layer."""
+    wl = sess.wl
+    s = 2 if wl.dtype.itemsize == 2 else 4
+    B, Hkv, Hq, d, P = sess.B, sess.Hkv, sess.Hq, sess.d, sess.P
+    pages = sum((n + P - 1) // P for n in rows_now)
+    q = B * Hq * d * s
+    summaries = Hkv * wl.k1 * pages * 2 * s
+    kv = per_head_rows * d * 2 * s
+    out = B * Hq * d * 4
+    append = B * 3 * Hkv * d * 2 * s
+    return (q + summaries + kv + out + append) * sess.n_layers, kv + q + out
+
+
+def cpu_baseline(wl, sess, budget_s: float):
+    """The oracle's decode step (summary append + HSA) on the host cores, on a
+    bounded sample: layer 0 of every sequence and KV head, caches of the same
+    shapes drawn by the generator, repeated until about budget_s seconds."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_kv_cache_hsa_amd import synth
+
+    B, Hkv, G, d, P = sess.B, sess.Hkv, sess.G, sess.d, sess.P
+    units = []
+    for b in range(B):
+        n = sess.keep[b]
+        cap = n + 64
+        for h in range(Hkv):
+            rows = synth.gaussian_rows(wl.seed, ("cpu-baseline", b, h), 2, cap, d)
+            k = synth.to_bits(rows[0].to(wl.dtype))
+            v = synth.to_bits(rows[1].to(wl.dtype))
+            np_ = (cap + P - 1) // P
+            smax = np.zeros((np_, d), k.dtype)
+            smin = np.zeros((np_, d), k.dtype)
+            oracle.summaries_append(k, 0, n, P, smax, smin)
+            q = synth.to_bits(synth.randn((G, d), wl.seed, "cpu-q", b, h).to(wl.dtype))
+            units.append([k, v, q, smax, smin, n])
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        for u in units:
+            k, v, q, smax, smin, n = u
+            oracle.summaries_append(k, n, n + 1, P, smax, smin)
+            oracle.hsa_group(q, k, v, smax, smin, n + 1, P, wl.k1, wl.k2, sess.scale)
+            u[5] = n + 1
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= 60:
+            break
+    per_layer_step = el / steps
+    return {"value": 1.0 / (per_layer_step * sess.n_layers), "unit": "steps/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{steps} decode steps of layer 0 only (all {B} sequences x {Hkv} KV "
+                      f"heads, caches of the workload's kept sizes), scaled to "
+                      f"{sess.n_layers} layers; {el:.1f} s single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-graph", action="store_true", help="enqueue steps eagerly")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path has no multi-GPU leg "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_kv_cache_hsa_amd import rkv, workloads
+    from sparse_kv_cache_hsa_amd.session import Session
+
+    rkv.load_library()
+    wl = workloads.ALL[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, W = args.steps, args.warmup
+    log(f"[bench] workload {wl.name}: {wl.description}")
+    sess = Session(wl, extra_rows=K + W, device=dev)
+    log(f"[bench] keep per sequence {min(sess.keep)}..{max(sess.keep)}, max_pages "
+        f"{sess.max_pages}, blocks {sess.num_blocks}")
+
+    # ---- stage 1 (prefill eviction), per layer --------------------------------
+    ev_ms = []
+    ews = sess.evict_workspace() if wl.evicts else None
+    for l in range(sess.n_layers):
+        t = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        sess.prefill_layer(l, ws=ews, timer=t)
+        torch.cuda.synchronize()
+        ev_ms.append(t[0].elapsed_time(t[1]))
+    del ews
+    torch.cuda.empty_cache()
+    log(f"[bench] prefill done: {sum(ev_ms):.1f} ms over {sess.n_layers} layers")
+
+    # ---- decode inputs and graphs ------------------------------------------
+    inputs = sess.make_inputs(W + K)
+    torch.cuda.synchronize()
+    graphs = []
+    if not args.no_graph:
+        for s in range(W + K):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                sess.step(inputs[s])
+            graphs.append(gph)
+        torch.cuda.synchronize()
+        log(f"[bench] captured {len(graphs)} step graphs")
+
+    def run(s):
+        if graphs:
+            graphs[s].replay()
+        else:
+            sess.step(inputs[s])
+
+    for s in range(W):
+        run(s)
+    torch.cuda.synchronize()
+    sess.advance(W)
+    rows_at_start = list(sess.rows)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for s in range(W, W + K):
+        run(s)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    sess.advance(K)
+    ms_step = ms_total / K
+    log(f"[bench] {K} steps in {ms_total:.2f} ms -> {ms_step * 1e3:.1f} us/step")
+
+    # attended rows of the last step (page_idx of every layer are current)
+    rows_last = sess.rows
+    per_head_rows = [attended_rows(sess, sess.page_idx[l], rows_last) for l in range(sess.n_layers)]
+    attended_seq_layer = sum(per_head_rows) / sess.Hkv       # per (sequence, layer)
+    step_b, attend_b0 = step_bytes(sess, rows_last, per_head_rows[0])
+
+    # ---- dominant kernel (attention) timed alone with events ----------------
+    # The queue is pre-filled with a spin so every launch below runs back to
+    # back; select first so that page_idx is current for every layer.
+    per_layer, _, n_new = inputs[W + K - 1]
+    for l in range(sess.n_layers):
+        rkv.rkv_hsa_select(sess.g, per_layer[l][2], n_new, sess.P, sess.summ[l], wl.k1, wl.k2,
+                           sess.page_idx[l], sess.ws)
+    torch.cuda.synchronize()
+    reps = 3
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps * sess.n_layers)]
+    torch.cuda._sleep(50_000_000)
+    i = 0
+    for _ in range(reps):
+        for l in range(sess.n_layers):
+            evs[i][0].record()
+            rkv.rkv_hsa_attend(sess.g, per_layer[l][2], sess.caches[l], n_new, sess.page_idx[l],
+                               wl.k2, sess.scale, sess.out, sess.ws)
+            evs[i][1].record()
+            i += 1
+    torch.cuda.synchronize()
+    att_us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    att_avg_us = sum(att_us) / len(att_us)
+    att_bytes = [attended_rows(sess, sess.page_idx[l], sess.rows) * sess.d * 2 * 2 +
+                 sess.B * sess.Hq * sess.d * (2 + 4) for l in range(sess.n_layers)]
+    att_bytes_avg = sum(att_bytes) / len(att_bytes)
+    att_gbs = att_bytes_avg / (att_avg_us * 1e-6) / 1e9
+    log(f"[bench] attention kernel: avg {att_avg_us:.2f} us, median {att_us[len(att_us) // 2]:.2f}"
+        f" us, {att_bytes_avg / 1e6:.2f} MB/launch -> {att_gbs:.0f} GB/s")
+
+    steps_per_s = 1e3 / ms_step
+    result = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype.itemsize == 2 else "f32",
+        "data": "synthetic (seeded Gaussian K/V with outlier channels, RoPE'd; no model weights)",
+        "attended_tokens_per_s": round(steps_per_s * attended_seq_layer, 1),
+        "step_hbm_bytes": step_b,
+        "step_hbm_gbs": round(step_b / (ms_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_b / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "stage1": {"ms_total": round(sum(ev_ms), 3), "ms_per_layer": round(sum(ev_ms) / len(ev_ms), 3),
+                   "batch_per_call": sess.B},
+        "config": {"workload": wl.name, "layers": sess.n_layers, "batch": sess.B,
+                   "q_heads": sess.Hq, "kv_heads": sess.Hkv, "head_dim": sess.d,
+                   "page_size": sess.P, "k1": wl.k1, "k2": wl.k2,
+                   "prompt_len_min": min(sess.prompt_lens), "prompt_len_max": max(sess.prompt_lens),
+                   "kept_rows_min": min(sess.keep), "kept_rows_max": max(sess.keep),
+                   "graph": not args.no_graph, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": "attend_kernel", "achieved": round(att_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(att_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(att_avg_us, 3),
+                     "bytes_per_launch": int(att_bytes_avg)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host ...")
+        result["cpu_baseline"] = cpu_baseline(wl, sess, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
