@@ -42,18 +42,19 @@ def attended_rows(sess, layer_page_idx, rows_now):
 
 
 def step_bytes(sess, rows_now, per_head_rows):
-    """Algorithmic HBM bytes of one decode step over every layer.
-    per_head_rows: attended rows summed over (sequence, KV head) of a layer."""
+    """Algorithmic HBM bytes of one decode step over every layer, and the
+    attention share (gathered K/V + q + out) of layer 0.
+    per_head_rows[l]: attended rows of layer l summed over (sequence, KV head)."""
     wl = sess.wl
     s = 2 if wl.dtype.itemsize == 2 else 4
     B, Hkv, Hq, d, P = sess.B, sess.Hkv, sess.Hq, sess.d, sess.P
     pages = sum((n + P - 1) // P for n in rows_now)
     q = B * Hq * d * s
     summaries = Hkv * wl.k1 * pages * 2 * s
-    kv = per_head_rows * d * 2 * s
+    kv = [r * d * 2 * s for r in per_head_rows]
     out = B * Hq * d * 4
     append = B * 3 * Hkv * d * 2 * s
-    return (q + summaries + kv + out + append) * sess.n_layers, kv + q + out
+    return (q + summaries + out + append) * sess.n_layers + sum(kv), kv[0] + q + out
 
 
 def cpu_baseline(wl, sess, budget_s: float):
@@ -166,7 +167,6 @@ def main():
         run(s)
     torch.cuda.synchronize()
     sess.advance(W)
-    rows_at_start = list(sess.rows)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
@@ -183,37 +183,46 @@ def main():
     rows_last = sess.rows
     per_head_rows = [attended_rows(sess, sess.page_idx[l], rows_last) for l in range(sess.n_layers)]
     attended_seq_layer = sum(per_head_rows) / sess.Hkv       # per (sequence, layer)
-    step_b, attend_b0 = step_bytes(sess, rows_last, per_head_rows[0])
+    step_b, attend_b0 = step_bytes(sess, rows_last, per_head_rows)
+    log(f"[bench] algorithmic bytes per step {step_b / 1e9:.3f} GB, attended rows per "
+        f"(sequence, layer) {attended_seq_layer:.1f}")
 
-    # ---- dominant kernel (attention) timed alone with events ----------------
-    # The queue is pre-filled with a spin so every launch below runs back to
-    # back; select first so that page_idx is current for every layer.
+    # ---- dominant kernel, timed alone ---------------------------------------
+    # Fused path: a step is one decode_kernel launch per layer, and replaying
+    # the last step's graph is idempotent (same row, same values, same
+    # summaries), so per-launch time = replay time / (replays * layers).
+    # Split path: the attention launches of every layer, captured alone.
     per_layer, _, n_new = inputs[W + K - 1]
-    for l in range(sess.n_layers):
-        rkv.rkv_hsa_select(sess.g, per_layer[l][2], n_new, sess.P, sess.summ[l], wl.k1, wl.k2,
-                           sess.page_idx[l], sess.ws)
-    torch.cuda.synchronize()
-    reps = 3
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps * sess.n_layers)]
-    torch.cuda._sleep(50_000_000)
-    i = 0
-    for _ in range(reps):
+    fused = rkv.fused_path(sess.g, sess.B, sess.P, sess.max_pages, wl.k2)
+    reps = 20
+    if fused and graphs:
+        kernel = "decode_kernel (append + select + attend, one launch per layer)"
+        gph = graphs[W + K - 1]
+        bytes_launch = step_b / sess.n_layers
+    else:
+        kernel = "attend_kernel"
         for l in range(sess.n_layers):
-            evs[i][0].record()
-            rkv.rkv_hsa_attend(sess.g, per_layer[l][2], sess.caches[l], n_new, sess.page_idx[l],
-                               wl.k2, sess.scale, sess.out, sess.ws)
-            evs[i][1].record()
-            i += 1
+            rkv.rkv_hsa_select(sess.g, per_layer[l][2], n_new, sess.P, sess.summ[l], wl.k1,
+                               wl.k2, sess.page_idx[l], sess.ws)
+        torch.cuda.synchronize()
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            for l in range(sess.n_layers):
+                rkv.rkv_hsa_attend(sess.g, per_layer[l][2], sess.caches[l], n_new,
+                                   sess.page_idx[l], wl.k2, sess.scale, sess.out, sess.ws)
+        bytes_launch = attend_b0
+    gph.replay()
     torch.cuda.synchronize()
-    att_us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-    att_avg_us = sum(att_us) / len(att_us)
-    att_bytes = [attended_rows(sess, sess.page_idx[l], sess.rows) * sess.d * 2 * 2 +
-                 sess.B * sess.Hq * sess.d * (2 + 4) for l in range(sess.n_layers)]
-    att_bytes_avg = sum(att_bytes) / len(att_bytes)
-    att_gbs = att_bytes_avg / (att_avg_us * 1e-6) / 1e9
-    log(f"[bench] attention kernel: avg {att_avg_us:.2f} us, median {att_us[len(att_us) // 2]:.2f}"
-        f" us, {att_bytes_avg / 1e6:.2f} MB/launch -> {att_gbs:.0f} GB/s")
+    k0, k1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record()
+    for _ in range(reps):
+        gph.replay()
+    k1e.record()
+    torch.cuda.synchronize()
+    launch_us = k0.elapsed_time(k1e) * 1e3 / (reps * sess.n_layers)
+    kern_gbs = bytes_launch / (launch_us * 1e-6) / 1e9
+    log(f"[bench] {kernel}: {launch_us:.2f} us/launch, {bytes_launch / 1e6:.2f} MB/launch -> "
+        f"{kern_gbs:.0f} GB/s")
 
     steps_per_s = 1e3 / ms_step
     result = {
@@ -241,10 +250,10 @@ def main():
                    "prompt_len_min": min(sess.prompt_lens), "prompt_len_max": max(sess.prompt_lens),
                    "kept_rows_min": min(sess.keep), "kept_rows_max": max(sess.keep),
                    "graph": not args.no_graph, "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "kernel": "attend_kernel", "achieved": round(att_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(att_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(att_avg_us, 3),
-                     "bytes_per_launch": int(att_bytes_avg)},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(kern_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(launch_us, 3),
+                     "bytes_per_launch": int(bytes_launch)},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host ...")

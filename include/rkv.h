@@ -194,7 +194,7 @@ int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,
  * n = 0 selects nothing and writes zeros.
  *
  * Arguments
- *   q            : device [B][Hq][d] decode queries.
+ *   q            : device [B][Hq][d] decode queries, 16-byte aligned.
  *   seq_lens     : device [B] int32 rows per sequence (current token
  *                  included); clamped to [0, max_pages * P].
  *   summaries    : device [B][Hkv][2][d][max_pages], current for seq_lens.
@@ -207,7 +207,8 @@ int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,
  *   scale        : logit scale (normally 1/sqrt(d)), finite and > 0.
  *   out          : device [B][Hq][d] fp32.
  *   ws, ws_bytes : device workspace of at least rkv_hsa_workspace_bytes(...)
- *                  for the same shapes.
+ *                  for the same shapes; calls sharing one workspace must be
+ *                  ordered on one stream.
  * rkv_hsa_decode = rkv_hsa_select followed by rkv_hsa_attend on `stream`.
  * Errors: RKV_EINVAL, RKV_EUNSUPPORTED, RKV_EWORKSPACE, RKV_EHIP. */
 size_t rkv_hsa_workspace_bytes(const rkv_gqa *g, int32_t B, int32_t page_size,
@@ -226,6 +227,27 @@ int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                    const void *summaries, int32_t k1, int32_t k2, float scale, float *out,
                    int32_t *chan_idx, int32_t *page_idx, float *page_scores, void *ws,
                    size_t ws_bytes, void *stream);
+
+/* ---- one decode step of one layer ---------------------------------------- */
+/* The per-layer hot path: append the new token, then HSA decode.  With
+ * n = seq_lens[b] (the new token included), row n-1 of every (sequence, KV
+ * head) is written from k_new/v_new and folded into the summary of its page
+ * ([P3] "Evidence": incremental update == rebuild), then selection and
+ * attention run exactly as rkv_hsa_decode.  Equivalent to
+ * rkv_append_summaries(n-1 -> n, copying k_new/v_new) followed by
+ * rkv_hsa_decode, with identical results.
+ *   k_new, v_new : device [B][Hkv][d], or both NULL (no append: this is then
+ *                  rkv_hsa_decode).
+ *   summaries    : current for rows [0, n-1) on entry, for [0, n) on return.
+ * When the batch fills the chip (B * Hkv >= 192, G <= 4, G * d <= 512,
+ * max_pages <= 2048, k2 * P <= 2048) the whole step is a single kernel, one
+ * 16-wave block per (sequence, KV head); otherwise the standalone kernels run
+ * in sequence.  Other arguments and errors as for rkv_hsa_decode. */
+int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
+                    const void *k_new, const void *v_new, const rkv_paged_cache *cache,
+                    const int32_t *seq_lens, void *summaries, int32_t k1, int32_t k2,
+                    float scale, float *out, int32_t *chan_idx, int32_t *page_idx,
+                    float *page_scores, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

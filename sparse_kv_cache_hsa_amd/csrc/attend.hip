@@ -1,234 +1,105 @@
-// attend.hip -- exact attention over the rows of the selected pages.
+// attend.hip -- exact attention over the rows of the selected pages (the
+// standalone second half of HSA decode; the fused decode kernel covers the
+// common case in one launch).
 //
-// RocketKV's second stage attends exactly over the tokens it selected
-// ("RocketKV-adapted -- Two-Stage Compression", "Adaptation notes": every row
-// of a selected page takes part).  The work is an HBM stream of whole K/V
-// page slices (P rows x d contiguous per KV head) at about 4 flop per byte,
-// far below the vector-ALU ridge, so it runs on the vector ALU in fp32
-// (bf16 widened exactly), not on MFMA.
-//
-// Mapping (gfx950, 64-lane waves)
-//   - A block (4 waves) handles one (sequence, KV head, split); a split is a
-//     contiguous range of the selected-page list.  The G query heads of the
-//     group share every K/V load (GQA reuse in registers).
-//   - A row of d elements is read by LPR lanes with one 16-byte load each;
-//     a wave reads RPW = 64/LPR rows per load and keeps U such loads of K and
-//     V in flight.
-//   - Dot products are finished with xor-shuffles inside the LPR lanes of a
-//     row; each row group keeps an online-softmax state (max, sum, acc) in
-//     the log2 domain (the query is pre-scaled by scale*log2(e)).
-//   - States are merged across row groups (shuffles), waves (LDS) and, when
-//     there is more than one split, across splits by merge_kernel in a fixed
-//     order, so results do not depend on scheduling.
+// A block handles one (sequence, KV head, split); a split is a range of the
+// selected-page list.  At block start every row of the block's pages is
+// resolved once (page table, validity) into an LDS row table, then the
+// streaming core (attend_core.h) reads whole K/V rows with 16-byte loads and
+// keeps an online softmax per query head.  With more than one split, each
+// block writes (max, sum, acc) to the workspace and a small merge kernel
+// combines the splits in split order.  (Merging inside the kernel through an
+// arrival counter needs a device-scope release per block, which on this chip
+// writes back the whole L2 and costs far more than the extra launch.)
 #include <stdlib.h>
 
-#include "rkv_internal.h"
+#include "attend_core.h"
 
 namespace rkv {
 namespace {
 
-constexpr int kAttBlock = 256;
-constexpr int kAttNW = kAttBlock / kWave;
-constexpr int kMaxPPB = 1024;
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxRows = 2048;  // rows resolved per block (LDS table)
 
-template <typename T, int D, int G>
-__global__ void __launch_bounds__(kAttBlock)
-attend_kernel(int Hkv, int P, int max_pages, int64_t num_blocks, const int32_t *page_table,
-              const T *k_pool, const T *v_pool, const T *q, const int32_t *seq_lens,
-              const int32_t *page_idx, int k2, int ppb, int n_splits, float qscale, float *out,
-              float *part) {
-    constexpr int EPL = Vec16<T>::N;
-    constexpr int LPR = D / EPL;
-    constexpr int RPW = kWave / LPR;
-    constexpr int U = 4;
-    constexpr int NW = kAttNW;
-    __shared__ int32_t blk_s[kMaxPPB];
-    __shared__ int32_t row0_s[kMaxPPB];
-    __shared__ float wm[NW][G], wl[NW][G];
-    __shared__ float wacc[NW][G][D];
+struct AttArgs {
+    int Hkv, P, max_pages, k2, ppb, n_splits;
+    int64_t num_blocks;
+    const int32_t *page_table, *seq_lens, *page_idx;
+    float qscale;
+    float *out, *part;
+};
+
+template <typename T, int D, int G, int NW, int U, bool PIPE>
+__global__ void __launch_bounds__(NW *kWave)
+attend_kernel(AttArgs a, const T *k_pool, const T *v_pool, const T *q) {
+    using Core = AttendCore<T, D, G, NW, U, PIPE>;
+    constexpr int BLOCK = NW * kWave;
+    __shared__ uint32_t row_s[kMaxRows];
+    __shared__ typename Core::Shared sh;
 
     const int b = blockIdx.z, h = blockIdx.y, sp = blockIdx.x, tid = threadIdx.x;
-    const int64_t bh = (int64_t)b * Hkv + h;
-    const int64_t cap = (int64_t)max_pages * P;
-    const int64_t n = min<int64_t>(max<int64_t>(seq_lens[b], 0), cap);
+    const int P = a.P;
+    const int64_t bh = (int64_t)b * a.Hkv + h;
+    const int64_t cap = (int64_t)a.max_pages * P;
+    const int64_t n = min<int64_t>(max<int64_t>(a.seq_lens[b], 0), cap);
     const int NP = (int)((n + P - 1) / P);
-    const int nsel = min(k2, NP);
-    const int i0 = sp * ppb;
-    const int npg = max(0, min(i0 + ppb, nsel) - i0);
-
-    for (int i = tid; i < npg; i += kAttBlock) {
-        const int32_t pg = page_idx[bh * k2 + i0 + i];
-        int32_t blk = -1;
-        if (pg >= 0 && pg < NP) blk = page_table[(int64_t)b * max_pages + pg];
-        if (blk < 0 || blk >= num_blocks) blk = -1;
-        blk_s[i] = blk;
-        row0_s[i] = pg * P;
-    }
-    __syncthreads();
-
-    const int lane = tid & (kWave - 1), w = tid / kWave;
-    const int sub = lane % LPR, rsub = lane / LPR;
-
-    float qv[G][EPL];
-#pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            qv[j][e] = Elem<T>::ld(q, (bh * G + j) * D + sub * EPL + e) * qscale;
-
-    float m[G], l[G], acc[G][EPL];
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-        m[j] = -INFINITY;
-        l[j] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[j][e] = 0.0f;
-    }
-
+    const int nsel = min(a.k2, NP);
+    const int i0 = sp * a.ppb;
+    const int npg = max(0, min(i0 + a.ppb, nsel) - i0);
     const int nrows = npg * P;
-    for (int base = w * U * RPW; base < nrows; base += NW * U * RPW) {
-        uint4 kr[U], vr[U];
-        bool valid[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int f = base + u * RPW + rsub;
-            valid[u] = false;
-            kr[u] = make_uint4(0u, 0u, 0u, 0u);
-            vr[u] = make_uint4(0u, 0u, 0u, 0u);
-            if (f < nrows) {
-                const int pi = f / P;
-                const int slot = f - pi * P;
-                const int32_t blk = blk_s[pi];
-                if (blk >= 0 && (int64_t)row0_s[pi] + slot < n) {
-                    valid[u] = true;
-                    const int64_t off = (((int64_t)blk * Hkv + h) * P + slot) * D + sub * EPL;
-                    kr[u] = *(const uint4 *)(k_pool + off);
-                    vr[u] = *(const uint4 *)(v_pool + off);
-                }
-            }
-        }
-        float sc[U][G];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float kf[EPL];
-            Vec16<T>::unpack(kr[u], kf);
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                float p = 0.0f;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(qv[j][e], kf[e], p);
-                sc[u][j] = p;
-            }
-        }
-#pragma unroll
-        for (int off = LPR / 2; off >= 1; off >>= 1)
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int j = 0; j < G; ++j) sc[u][j] += __shfl_xor(sc[u][j], off, kWave);
 
-        float vf[U][EPL];
-#pragma unroll
-        for (int u = 0; u < U; ++u) Vec16<T>::unpack(vr[u], vf[u]);
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            float mn = m[j];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (valid[u]) mn = fmaxf(mn, sc[u][j]);
-            const float corr = exp2_diff(m[j], mn);
-            m[j] = mn;
-            l[j] *= corr;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[j][e] *= corr;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (valid[u]) {
-                    const float p = exp2f(sc[u][j] - mn);
-                    l[j] += p;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) acc[j][e] = __builtin_fmaf(p, vf[u][e], acc[j][e]);
-                }
-            }
+    for (int f = tid; f < nrows; f += BLOCK) {
+        const int pi = f / P, slot = f - pi * P;
+        const int32_t pg = a.page_idx[bh * a.k2 + i0 + pi];
+        uint32_t r = kBadRow;
+        if (pg >= 0 && pg < NP && (int64_t)pg * P + slot < n) {
+            const int32_t blk = a.page_table[(int64_t)b * a.max_pages + pg];
+            if (blk >= 0 && blk < a.num_blocks) r = (uint32_t)(((int64_t)blk * a.Hkv + h) * P + slot);
         }
+        row_s[f] = r;
     }
-
-    // merge the RPW row groups of the wave
-#pragma unroll
-    for (int off = LPR; off < kWave; off <<= 1) {
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const float mo = __shfl_xor(m[j], off, kWave);
-            const float lo = __shfl_xor(l[j], off, kWave);
-            const float mn = fmaxf(m[j], mo);
-            const float c1 = exp2_diff(m[j], mn), c2 = exp2_diff(mo, mn);
-            l[j] = l[j] * c1 + lo * c2;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                const float ao = __shfl_xor(acc[j][e], off, kWave);
-                acc[j][e] = acc[j][e] * c1 + ao * c2;
-            }
-            m[j] = mn;
-        }
-    }
-    if (rsub == 0) {
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            if (sub == 0) {
-                wm[w][j] = m[j];
-                wl[w][j] = l[j];
-            }
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) wacc[w][j][sub * EPL + e] = acc[j][e];
-        }
-    }
+    Core core;
+    core.init(q, bh, a.qscale);
     __syncthreads();
-
-    // merge the waves; one thread per (head, channel)
-    for (int t = tid; t < G * D; t += kAttBlock) {
-        const int j = t / D, c = t % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww][j]);
-        float Lsum = 0.0f, A = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const float cw = exp2_diff(wm[ww][j], M);
-            Lsum += wl[ww][j] * cw;
-            A += wacc[ww][j][c] * cw;
-        }
-        if (n_splits == 1) {
-            out[(bh * G + j) * D + c] = Lsum > 0.0f ? A / Lsum : 0.0f;
-        } else {
-            float *pp = part + ((bh * n_splits + sp) * G + j) * (D + 2);
+    core.stream(row_s, nrows, k_pool, v_pool);
+    core.to_shared(sh);
+    __syncthreads();
+    if (a.n_splits == 1) {
+        Core::combine(sh, [&](int j, int c, float M, float Ls, float A) {
+            a.out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
+        });
+    } else {
+        float *base = a.part + (bh * a.n_splits + sp) * G * (D + 2);
+        Core::combine(sh, [&](int j, int c, float M, float Ls, float A) {
+            float *pp = base + j * (D + 2);
             pp[c] = A;
             if (c == 0) {
                 pp[D] = M;
-                pp[D + 1] = Lsum;
+                pp[D + 1] = Ls;
             }
-        }
+        });
     }
 }
 
+// Combines the splits of every (sequence, KV head) in split order.
 template <int D, int G>
-__global__ void __launch_bounds__(kAttBlock)
+__global__ void __launch_bounds__(256)
 attend_merge_kernel(int Hkv, int n_splits, const float *part, float *out) {
     const int b = blockIdx.y, h = blockIdx.x;
     const int64_t bh = (int64_t)b * Hkv + h;
-    for (int t = threadIdx.x; t < G * D; t += kAttBlock) {
+    for (int t = threadIdx.x; t < G * D; t += 256) {
         const int j = t / D, c = t % D;
+        const float *base_p = part + (bh * n_splits * G + j) * (D + 2);
+        const int64_t stride = (int64_t)G * (D + 2);
         float M = -INFINITY;
-        for (int s = 0; s < n_splits; ++s)
-            M = fmaxf(M, part[((bh * n_splits + s) * G + j) * (D + 2) + D]);
-        float Lsum = 0.0f, A = 0.0f;
+        for (int s = 0; s < n_splits; ++s) M = fmaxf(M, base_p[s * stride + D]);
+        float Ls = 0.0f, A = 0.0f;
         for (int s = 0; s < n_splits; ++s) {
-            const float *pp = part + ((bh * n_splits + s) * G + j) * (D + 2);
+            const float *pp = base_p + s * stride;
             const float cw = exp2_diff(pp[D], M);
-            Lsum += pp[D + 1] * cw;
+            Ls += pp[D + 1] * cw;
             A += pp[c] * cw;
         }
-        out[(bh * G + j) * D + c] = Lsum > 0.0f ? A / Lsum : 0.0f;
+        out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
     }
 }
 
@@ -237,21 +108,40 @@ int env_int(const char *name, int dflt) {
     return (v && *v) ? atoi(v) : dflt;
 }
 
+// Kernel variants: (waves per block, row loads per iteration, pipelined).
+constexpr int kVariantWaves[4] = {4, 8, 16, 16};
+
 template <typename T, int D, int G>
 int launch_t(const rkv_gqa &g, int B, const void *q, const rkv_paged_cache &c,
              const int32_t *seq_lens, const int32_t *page_idx, int k2, float scale, float *out,
              void *ws, hipStream_t s) {
     const AttendPlan pl = plan_attend(g, B, c.page_size, k2);
+    AttArgs a;
+    a.Hkv = g.n_kv_heads;
+    a.P = c.page_size;
+    a.max_pages = c.max_pages;
+    a.k2 = k2;
+    a.ppb = pl.pages_per_block;
+    a.n_splits = pl.n_splits;
+    a.num_blocks = c.num_blocks;
+    a.page_table = c.page_table;
+    a.seq_lens = seq_lens;
+    a.page_idx = page_idx;
+    a.qscale = scale * kLog2e;
+    a.out = out;
+    a.part = (float *)ws;
     dim3 grid(pl.n_splits, g.n_kv_heads, B);
-    float *part = (float *)ws;
-    attend_kernel<T, D, G><<<grid, kAttBlock, 0, s>>>(
-        g.n_kv_heads, c.page_size, c.max_pages, c.num_blocks, c.page_table, (const T *)c.k_pool,
-        (const T *)c.v_pool, (const T *)q, seq_lens, page_idx, k2, pl.pages_per_block,
-        pl.n_splits, scale * kLog2e, out, part);
+    const T *kp = (const T *)c.k_pool, *vp = (const T *)c.v_pool, *qp = (const T *)q;
+    switch (pl.variant) {
+        case 1: attend_kernel<T, D, G, 8, 2, true><<<grid, 8 * kWave, 0, s>>>(a, kp, vp, qp); break;
+        case 2: attend_kernel<T, D, G, 16, 4, false><<<grid, 16 * kWave, 0, s>>>(a, kp, vp, qp); break;
+        case 3: attend_kernel<T, D, G, 16, 2, true><<<grid, 16 * kWave, 0, s>>>(a, kp, vp, qp); break;
+        default: attend_kernel<T, D, G, 4, 4, false><<<grid, 4 * kWave, 0, s>>>(a, kp, vp, qp); break;
+    }
     int st = launch_status();
     if (st != RKV_OK || pl.n_splits == 1) return st;
-    attend_merge_kernel<D, G><<<dim3(g.n_kv_heads, B), kAttBlock, 0, s>>>(g.n_kv_heads,
-                                                                         pl.n_splits, part, out);
+    attend_merge_kernel<D, G><<<dim3(g.n_kv_heads, B), 256, 0, s>>>(g.n_kv_heads, pl.n_splits,
+                                                                   a.part, out);
     return launch_status();
 }
 
@@ -272,20 +162,36 @@ int dispatch_g(const rkv_gqa &g, int B, const void *q, const rkv_paged_cache &c,
 
 AttendPlan plan_attend(const rkv_gqa &g, int B, int P, int k2) {
     const int units = B * g.n_kv_heads;
+    const int max_ppb = kMaxRows / P > 0 ? kMaxRows / P : 1;
+    AttendPlan p;
+    int variant = env_int("RKV_ATTEND_VARIANT", -1);
+    const bool wide_ok = g.group * g.head_dim <= 512;  // wide blocks keep G*D per wave in LDS
+    if (variant < 0 || variant > 3) {
+        // One wide block per (sequence, head) once the batch fills the chip;
+        // otherwise 4-wave blocks over splits of the page list.
+        variant = (units >= 192 && wide_ok && (int64_t)k2 * P <= kMaxRows) ? 2 : 0;
+    }
+    if (kVariantWaves[variant] > 4 && !wide_ok) variant = 0;
+    const int waves = kVariantWaves[variant];
     int ppb = env_int("RKV_ATTEND_PPB", 0);
     if (ppb <= 0) {
-        // >= 64 rows per block (one full pass of the 4 waves), and about
-        // 1024 blocks in total when the batch allows it.
-        const int min_rows = (64 + P - 1) / P;
-        const int spread = (int)(((int64_t)k2 * units + 1023) / 1024);
-        ppb = min_rows > spread ? min_rows : spread;
+        if (waves == 16) {
+            ppb = k2;
+        } else {
+            // about 1024 blocks, with at least one full pass of the block's
+            // waves (64 rows each) per split
+            const int min_rows = (64 * waves + P - 1) / P;
+            const int spread = (int)(((int64_t)k2 * units * waves / 4 + 1023) / 1024);
+            ppb = min_rows > spread ? min_rows : spread;
+        }
     }
     if (ppb > k2) ppb = k2;
-    if (ppb > kMaxPPB) ppb = kMaxPPB;
+    if (ppb > max_ppb) ppb = max_ppb;
     if (ppb < 1) ppb = 1;
-    AttendPlan p;
     p.pages_per_block = ppb;
     p.n_splits = (k2 + ppb - 1) / ppb;
+    p.waves = waves;
+    p.variant = variant;
     return p;
 }
 

@@ -1,0 +1,266 @@
+// attend_core.h -- the streaming attention core shared by the split-K
+// attention kernel and the fused decode kernel.
+//
+// RocketKV's second stage attends exactly over the tokens of the selected
+// pages ("RocketKV-adapted -- Two-Stage Compression", "Adaptation notes").
+// The work is an HBM stream of K/V page slices at about 4 flop per byte, far
+// below the vector-ALU ridge, so it runs on the vector ALU in fp32 (bf16
+// widened exactly).
+//
+// Layout of the work inside a block of NW waves:
+//   - the block's rows are listed in an LDS table (row_s) of row units
+//     (block * Hkv + h) * P + slot, or kBadRow for rows that do not exist;
+//   - a row of d elements is read by LPR lanes with one 16-byte load each, a
+//     wave reads RPW = 64/LPR rows per load and U loads of K and of V per
+//     iteration; waves take iterations round-robin;
+//   - each lane holds its EPL channels of the G query heads (the G heads share
+//     every K/V load) and an online-softmax state per head in the log2 domain;
+//   - bf16 dot products use the packed bf16 dot instruction (exact products,
+//     fp32 accumulation) with the query kept as exact bf16 pairs and the
+//     scale*log2(e) factor applied to the finished dot product; fp32 inputs
+//     use fp32 multiply-adds with a pre-scaled query;
+//   - dot products are finished inside the LPR lanes of a row with DPP
+//     butterflies; at the end the row groups of a wave are merged with
+//     shuffles and the waves through LDS, in a fixed order.
+#pragma once
+
+#include <type_traits>
+
+#include "rkv_internal.h"
+
+namespace rkv {
+
+constexpr uint32_t kBadRow = 0xffffffffu;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// DPP lane permutes (gfx9 encodings).
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over the LPR consecutive lanes that share a row; every lane of the row
+// gets the same bits (each step adds a commutative pair).
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+    static_assert(LPR == 4 || LPR == 8 || LPR == 16 || LPR == 32, "lanes per row");
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    if constexpr (LPR >= 8) v += dpp<kDppHalfMirror>(v);
+    if constexpr (LPR >= 16) v += dpp<kDppMirror>(v);
+    if constexpr (LPR >= 32) v += __shfl_xor(v, 16, kWave);
+    return v;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <typename T, int D, int G, int NW, int U, bool PIPE>
+struct AttendCore {
+    static constexpr bool kPacked = std::is_same<T, uint16_t>::value;
+    static constexpr int EPL = Vec16<T>::N;  // channels per lane
+    static constexpr int LPR = D / EPL;      // lanes per row
+    static constexpr int RPW = kWave / LPR;  // rows per wave load
+    static constexpr int ROWS_IT = U * RPW;  // rows per wave iteration
+
+    struct Shared {
+        float wm[NW][G], wl[NW][G];
+        float wacc[NW][G][D];
+    };
+
+    float qv[G][EPL];       // fp32 inputs: pre-scaled query
+    uint32_t qp[G][4];      // bf16 inputs: query channel pairs, exact
+    float qs_;              // bf16 inputs: scale*log2(e)
+    float m[G], l[G], acc[G][EPL];
+    int lane, w, sub, rsub;
+
+    // q of the G heads sharing KV head bh, this lane's channels.
+    __device__ __forceinline__ void init(const T *q, int64_t bh, float qscale) {
+        lane = threadIdx.x & (kWave - 1);
+        w = threadIdx.x / kWave;
+        sub = lane % LPR;
+        rsub = lane / LPR;
+        qs_ = qscale;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const uint4 raw = *(const uint4 *)(q + (bh * G + j) * D + sub * EPL);
+            if constexpr (kPacked) {
+                qp[j][0] = raw.x;
+                qp[j][1] = raw.y;
+                qp[j][2] = raw.z;
+                qp[j][3] = raw.w;
+            } else {
+                Vec16<T>::unpack(raw, qv[j]);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) qv[j][e] *= qscale;
+            }
+            m[j] = -INFINITY;
+            l[j] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[j][e] = 0.0f;
+        }
+    }
+
+    __device__ __forceinline__ void issue(const uint32_t *row_s, int nrows, const T *k_pool,
+                                          const T *v_pool, int base, uint4 *kr, uint4 *vr,
+                                          bool *ok) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int f = base + u * RPW + rsub;
+            const uint32_t r = f < nrows ? row_s[f] : kBadRow;
+            ok[u] = r != kBadRow;
+            const int64_t off = (int64_t)(ok[u] ? r : 0u) * D + sub * EPL;
+            kr[u] = ok[u] ? *(const uint4 *)(k_pool + off) : make_uint4(0u, 0u, 0u, 0u);
+            vr[u] = ok[u] ? *(const uint4 *)(v_pool + off) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+
+    __device__ __forceinline__ void consume(const uint4 *kr, const uint4 *vr, const bool *ok) {
+        float sc[U][G];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (kPacked) {
+                const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    float p = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) p = dot2_bf16(qp[j][e], kw[e], p);
+                    sc[u][j] = row_sum<LPR>(p) * qs_;
+                }
+            } else {
+                float kf[EPL];
+                Vec16<T>::unpack(kr[u], kf);
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    float p = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) p = __builtin_fmaf(qv[j][e], kf[e], p);
+                    sc[u][j] = row_sum<LPR>(p);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float mn = m[j];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (ok[u]) mn = fmaxf(mn, sc[u][j]);
+            const float corr = exp2_diff(m[j], mn);
+            m[j] = mn;
+            float lj = l[j] * corr;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[j][e] *= corr;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                sc[u][j] = ok[u] ? exp2f(sc[u][j] - mn) : 0.0f;
+                lj += sc[u][j];
+            }
+            l[j] = lj;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[EPL];
+            Vec16<T>::unpack(vr[u], vf);
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[j][e] = __builtin_fmaf(sc[u][j], vf[e], acc[j][e]);
+        }
+    }
+
+    // Streams rows [0, nrows) of row_s (visible to the block).
+    __device__ __forceinline__ void stream(const uint32_t *row_s, int nrows, const T *k_pool,
+                                           const T *v_pool) {
+        const int step = NW * ROWS_IT;
+        if constexpr (PIPE) {
+            uint4 kn[U], vn[U];
+            bool okn[U];
+            int base = w * ROWS_IT;
+            issue(row_s, nrows, k_pool, v_pool, base, kn, vn, okn);
+            for (; base < nrows; base += step) {
+                uint4 kr[U], vr[U];
+                bool ok[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    kr[u] = kn[u];
+                    vr[u] = vn[u];
+                    ok[u] = okn[u];
+                }
+                if (base + step < nrows) issue(row_s, nrows, k_pool, v_pool, base + step, kn, vn, okn);
+                consume(kr, vr, ok);
+            }
+        } else {
+            for (int base = w * ROWS_IT; base < nrows; base += step) {
+                uint4 kr[U], vr[U];
+                bool ok[U];
+                issue(row_s, nrows, k_pool, v_pool, base, kr, vr, ok);
+                consume(kr, vr, ok);
+            }
+        }
+    }
+
+    // Merges the row groups of each wave and stores the waves' states in LDS.
+    // The caller synchronises the block before combine().
+    __device__ __forceinline__ void to_shared(Shared &sh) {
+#pragma unroll
+        for (int off = LPR; off < kWave; off <<= 1) {
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float mo = __shfl_xor(m[j], off, kWave);
+                const float lo = __shfl_xor(l[j], off, kWave);
+                const float mn = fmaxf(m[j], mo);
+                const float c1 = exp2_diff(m[j], mn), c2 = exp2_diff(mo, mn);
+                l[j] = l[j] * c1 + lo * c2;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const float ao = __shfl_xor(acc[j][e], off, kWave);
+                    acc[j][e] = acc[j][e] * c1 + ao * c2;
+                }
+                m[j] = mn;
+            }
+        }
+        if (rsub == 0) {
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                if (sub == 0) {
+                    sh.wm[w][j] = m[j];
+                    sh.wl[w][j] = l[j];
+                }
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) sh.wacc[w][j][sub * EPL + e] = acc[j][e];
+            }
+        }
+    }
+
+    // Combines the waves in wave order: fn(j, c, max, sum, acc) once per
+    // (head, channel) across the block.
+    template <typename Fn>
+    static __device__ __forceinline__ void combine(const Shared &sh, Fn fn) {
+        for (int t = threadIdx.x; t < G * D; t += NW * kWave) {
+            const int j = t / D, c = t % D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sh.wm[ww][j]);
+            float Ls = 0.0f, A = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const float cw = exp2_diff(sh.wm[ww][j], M);
+                Ls += sh.wl[ww][j] * cw;
+                A += sh.wacc[ww][j][c] * cw;
+            }
+            fn(j, c, M, Ls, A);
+        }
+    }
+};
+
+}  // namespace rkv

@@ -1,0 +1,253 @@
+// decode.hip -- one decode step of one layer in a single launch: append the
+// new token (K/V row and its page summary), rank channels, score pages, pick
+// the top-k2 pages and attend over them.
+//
+// The steps are those of RocketKV's decode path ("RocketKV-adapted --
+// Two-Stage Compression": "Where it sits" for the two-dimensional score bound,
+// "Adaptation notes" for whole-page selection, "Evidence" for the incremental
+// summary update).  One block of 16 waves owns one (sequence, KV head): the
+// chosen channels, page scores and page list never leave LDS, and the block's
+// attention phase starts as soon as its own selection is done, so a layer
+// costs one launch and one dependent chain of memory round trips instead of
+// three kernels.  Selection uses the same device code as the standalone
+// kernels (select_core.h), so its bits are identical; attention uses the
+// streaming core (attend_core.h).
+//
+// Used when the batch fills the chip (enough (sequence, head) units for
+// every CU) and the shapes fit LDS; otherwise the standalone append, select
+// and split-K attention kernels run in sequence.
+#include <stdlib.h>
+
+#include "attend_core.h"
+#include "select_core.h"
+
+namespace rkv {
+namespace {
+
+constexpr int kNW = 16;
+constexpr int kBlock = kNW * kWave;
+constexpr int kFusedMaxPages = 2048;
+constexpr int kFusedMaxRows = 2048;
+constexpr size_t kStageBytes = 64 * 1024;
+
+constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
+
+struct DecArgs {
+    int Hkv, P, max_pages, k1, k2;
+    int64_t num_blocks;
+    const int32_t *page_table, *seq_lens;
+    float qscale;
+    float *out;
+    int32_t *chan_out, *page_out;
+    float *score_out;
+};
+
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(kBlock)
+decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, T *v_pool,
+              T *summ) {
+    using Core = AttendCore<T, D, G, kNW, 4, false>;
+    constexpr size_t kKeyBytes = sizeof(uint64_t) * kFusedMaxPages;
+    constexpr size_t kRowBytes = sizeof(uint32_t) * kFusedMaxRows;
+    constexpr size_t kCoreBytes = sizeof(typename Core::Shared);
+    constexpr size_t kUnion = cmax(cmax(kStageBytes, kKeyBytes), cmax(kRowBytes, kCoreBytes));
+    __shared__ float qs[G][D];
+    __shared__ float qsel[G][D];
+    __shared__ int ch_s[D];
+    __shared__ T ovr_hi[D], ovr_lo[D];
+    __shared__ int32_t sel_s[RKV_MAX_K2];
+    __shared__ int32_t blk_s[kFusedMaxPages];
+    __shared__ int cnt_s[kBlock];
+    __shared__ uint32_t hist[256];
+    __shared__ int wave_tot[kNW];
+    __shared__ int sh[2];
+    // staged summaries or page keys (selection), then the row table
+    // (attention), then the waves' partial states (final merge): never live
+    // at the same time
+    __shared__ __align__(16) unsigned char u_s[kUnion];
+    T *stage = (T *)u_s;
+    uint64_t *comp_s = (uint64_t *)u_s;
+    uint32_t *row_s = (uint32_t *)u_s;
+    typename Core::Shared &csh = *(typename Core::Shared *)u_s;
+
+    const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+    const int P = a.P, k1 = a.k1, k2 = a.k2, max_pages = a.max_pages;
+    const int64_t bh = (int64_t)b * a.Hkv + h;
+    const int64_t cap = (int64_t)max_pages * P;
+    const int64_t n = min<int64_t>(max<int64_t>(a.seq_lens[b], 0), cap);
+    const int NP = (int)((n + P - 1) / P);
+    T *sm_max = summ + bh * 2 * D * max_pages;
+    T *sm_min = sm_max + (int64_t)D * max_pages;
+
+    // 1. append row n-1 and fold it into its page summary (first of equal
+    //    values kept: strict comparisons, as in a rebuild); keep the page's new
+    //    summary in LDS for this block's own scoring.  Meanwhile prefetch the
+    //    page table row and the queries.
+    const bool append = k_new != nullptr && n > 0;
+    const int p_new = append ? (int)((n - 1) / P) : -1;
+    if (append && tid < D) {
+        const int slot = (int)(n - 1 - (int64_t)p_new * P);
+        const int32_t blk = a.page_table[(int64_t)b * max_pages + p_new];
+        const T x = k_new[bh * D + tid];
+        const int64_t im = (int64_t)tid * max_pages + p_new;
+        T nmax = x, nmin = x;
+        if (slot != 0) {
+            const T omax = sm_max[im], omin = sm_min[im];
+            const float fx = Elem<T>::ld(&x, 0);
+            nmax = fx > Elem<T>::ld(&omax, 0) ? x : omax;
+            nmin = fx < Elem<T>::ld(&omin, 0) ? x : omin;
+        }
+        ovr_hi[tid] = nmax;
+        ovr_lo[tid] = nmin;
+        if (blk >= 0 && blk < a.num_blocks) {
+            const int64_t dst = (((int64_t)blk * a.Hkv + h) * P + slot) * D + tid;
+            k_pool[dst] = x;
+            v_pool[dst] = v_new[bh * D + tid];
+            sm_max[im] = nmax;
+            sm_min[im] = nmin;
+        }
+    }
+    for (int p = tid; p < NP; p += kBlock) blk_s[p] = a.page_table[(int64_t)b * max_pages + p];
+    load_group_q<T, D, G, kBlock>(q, bh, qs);
+    lds_barrier();
+
+    // 2. channels
+    rank_channels<D, G, kBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot);
+    if (a.chan_out && tid < k1) a.chan_out[bh * k1 + tid] = ch_s[tid];
+
+    // 3-4. page bounds and page top-k2.  The summaries of the chosen channels
+    //      are staged in LDS by the whole block when they fit; the page holding
+    //      the appended row takes this block's new summary from LDS (its
+    //      global stores need not have landed).
+    const int K = min(k2, NP);
+    constexpr int V = 16 / (int)sizeof(T);
+    const bool staged = (size_t)2 * k1 * ((NP + V - 1) / V * V) * sizeof(T) <= kStageBytes &&
+                        NP <= kBlock;
+    auto emit = [&](int o, int i) {
+        sel_s[o] = i;
+        if (a.page_out) a.page_out[bh * k2 + o] = i;
+    };
+    if (staged) {
+        const int npad = stage_summaries<T, kBlock>(sm_max, sm_min, max_pages, 0, NP, ch_s, k1, stage);
+        lds_barrier();
+        if (p_new >= 0 && tid < k1) {
+            stage[(int64_t)tid * npad + p_new] = ovr_hi[ch_s[tid]];
+            stage[(int64_t)(k1 + tid) * npad + p_new] = ovr_lo[ch_s[tid]];
+        }
+        lds_barrier();
+        uint64_t key = 0;
+        if (tid < NP) {
+            const float sc = staged_bound<T, D, G>(stage, npad, tid, k1, qsel);
+            key = composite_key(ordered_key(sc), tid);
+            if (a.score_out) a.score_out[bh * max_pages + tid] = sc;
+        }
+        lds_barrier();  // the staged rows are dead; their LDS takes the sorted keys
+        if (K > 0) sort_topk<kBlock>(key, NP, K, comp_s, wave_tot, emit);
+    } else {
+        for (int p = tid; p < NP; p += kBlock) {
+            float sc = page_bound<T, D, G>(sm_max, sm_min, max_pages, p, ch_s, k1, qsel);
+            if (p == p_new) sc = page_bound_ovr<T, D, G>(ch_s, k1, qsel, ovr_hi, ovr_lo);
+            comp_s[p] = composite_key(ordered_key(sc), p);
+            if (a.score_out) a.score_out[bh * max_pages + p] = sc;
+        }
+        lds_barrier();
+        topk_ascending<kBlock>(comp_s, NP, K, cnt_s, hist, sh, wave_tot, emit);
+    }
+    if (a.page_out)
+        for (int o = K + tid; o < k2; o += kBlock) a.page_out[bh * k2 + o] = -1;
+    lds_barrier();
+
+    // 5. resolve the rows of the selected pages, then stream them.  The full
+    //    barrier makes the appended K/V row (a global store of this block)
+    //    visible to every wave before any of them reads it.
+    const int nrows = K * P;
+    for (int f = tid; f < nrows; f += kBlock) {
+        const int pi = f / P, slot = f - pi * P;
+        const int32_t pg = sel_s[pi];
+        uint32_t r = kBadRow;
+        if ((int64_t)pg * P + slot < n) {
+            const int32_t blk = blk_s[pg];
+            if (blk >= 0 && blk < a.num_blocks) r = (uint32_t)(((int64_t)blk * a.Hkv + h) * P + slot);
+        }
+        row_s[f] = r;
+    }
+    Core core;
+    core.init(q, bh, a.qscale);
+    __syncthreads();
+    core.stream(row_s, nrows, k_pool, v_pool);
+    lds_barrier();  // the row table is dead; its LDS now takes the states
+    core.to_shared(csh);
+    lds_barrier();
+    Core::combine(csh, [&](int j, int c, float M, float Ls, float A) {
+        a.out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
+    });
+}
+
+template <typename T, int D, int G>
+void launch_t(int B, const rkv_gqa &g, const DecArgs &a, const void *q, const void *k_new,
+              const void *v_new, const rkv_paged_cache &c, void *summ, hipStream_t s) {
+    decode_kernel<T, D, G><<<dim3(g.n_kv_heads, B), kBlock, 0, s>>>(
+        a, (const T *)q, (const T *)k_new, (const T *)v_new, (T *)c.k_pool, (T *)c.v_pool,
+        (T *)summ);
+}
+
+template <typename T, int D>
+bool dispatch_g(int B, const rkv_gqa &g, const DecArgs &a, const void *q, const void *k_new,
+                const void *v_new, const rkv_paged_cache &c, void *summ, hipStream_t s) {
+    switch (g.group) {
+        case 1: launch_t<T, D, 1>(B, g, a, q, k_new, v_new, c, summ, s); return true;
+        case 2: launch_t<T, D, 2>(B, g, a, q, k_new, v_new, c, summ, s); return true;
+        case 4: launch_t<T, D, 4>(B, g, a, q, k_new, v_new, c, summ, s); return true;
+    }
+    return false;
+}
+
+int env_int(const char *name, int dflt) {
+    const char *v = getenv(name);
+    return (v && *v) ? atoi(v) : dflt;
+}
+
+}  // namespace
+
+bool fused_decode_ok(const rkv_gqa &g, int B, int P, int max_pages, int k2) {
+    if (g.group * g.head_dim > 512 || g.group > 4) return false;
+    if (max_pages > kFusedMaxPages || (int64_t)k2 * P > kFusedMaxRows) return false;
+    const int force = env_int("RKV_FUSED", -1);
+    if (force == 0) return false;
+    if (force == 1) return true;
+    return B * g.n_kv_heads >= 192;
+}
+
+int launch_decode_fused(const rkv_gqa &g, int dtype, int B, const void *q, const void *k_new,
+                        const void *v_new, const rkv_paged_cache &c, const int32_t *seq_lens,
+                        void *summaries, int k1, int k2, float scale, float *out,
+                        int32_t *chan_idx, int32_t *page_idx, float *page_scores,
+                        hipStream_t s) {
+    DecArgs a;
+    a.Hkv = g.n_kv_heads;
+    a.P = c.page_size;
+    a.max_pages = c.max_pages;
+    a.k1 = k1;
+    a.k2 = k2;
+    a.num_blocks = c.num_blocks;
+    a.page_table = c.page_table;
+    a.seq_lens = seq_lens;
+    a.qscale = scale * kLog2e;
+    a.out = out;
+    a.chan_out = chan_idx;
+    a.page_out = page_idx;
+    a.score_out = page_scores;
+    bool ok = false;
+    const int d = g.head_dim;
+    if (dtype == RKV_F32) {
+        if (d == 64) ok = dispatch_g<float, 64>(B, g, a, q, k_new, v_new, c, summaries, s);
+        else if (d == 128) ok = dispatch_g<float, 128>(B, g, a, q, k_new, v_new, c, summaries, s);
+    } else {
+        if (d == 64) ok = dispatch_g<uint16_t, 64>(B, g, a, q, k_new, v_new, c, summaries, s);
+        else if (d == 128) ok = dispatch_g<uint16_t, 128>(B, g, a, q, k_new, v_new, c, summaries, s);
+    }
+    if (!ok) return RKV_EUNSUPPORTED;
+    return launch_status();
+}
+
+}  // namespace rkv

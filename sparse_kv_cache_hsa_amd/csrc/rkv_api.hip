@@ -43,7 +43,7 @@ int check_select_args(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
     int st = check_gqa(g);
     if (st != RKV_OK) return st;
     if ((st = check_dtype(dtype)) != RKV_OK) return st;
-    if (B < 1 || B > 65535 || !q || !seq_lens) return RKV_EINVAL;
+    if (B < 1 || B > 65535 || !q || !seq_lens || !aligned16(q)) return RKV_EINVAL;
     if (P < 1 || max_pages < 1) return RKV_EINVAL;
     if (P > 256) return RKV_EUNSUPPORTED;
     if ((int64_t)max_pages * P > (int64_t)1 << 30) return RKV_EINVAL;
@@ -189,29 +189,47 @@ int rkv_hsa_attend(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                          (hipStream_t)stream);
 }
 
-int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
-                   const rkv_paged_cache *cache, const int32_t *seq_lens, const void *summaries,
-                   int32_t k1, int32_t k2, float scale, float *out, int32_t *chan_idx,
-                   int32_t *page_idx, float *page_scores, void *ws, size_t ws_bytes,
-                   void *stream) {
+int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
+                    const void *k_new, const void *v_new, const rkv_paged_cache *cache,
+                    const int32_t *seq_lens, void *summaries, int32_t k1, int32_t k2,
+                    float scale, float *out, int32_t *chan_idx, int32_t *page_idx,
+                    float *page_scores, void *ws, size_t ws_bytes, void *stream) {
     int st = check_gqa(g);
     if (st != RKV_OK) return st;
     if ((st = check_cache(cache)) != RKV_OK) return st;
     st = check_select_args(g, dtype, B, q, seq_lens, cache->page_size, cache->max_pages, k1, k2);
     if (st != RKV_OK) return st;
     if (!summaries || !out || !(scale > 0.0f) || !isfinite(scale)) return RKV_EINVAL;
+    if ((k_new == nullptr) != (v_new == nullptr)) return RKV_EINVAL;
     const size_t need = rkv_hsa_workspace_bytes(g, B, cache->page_size, cache->max_pages, k1, k2);
     if (!ws || ws_bytes < need) return RKV_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    if (fused_decode_ok(*g, B, cache->page_size, cache->max_pages, k2))
+        return launch_decode_fused(*g, dtype, B, q, k_new, v_new, *cache, seq_lens, summaries, k1,
+                                   k2, scale, out, chan_idx, page_idx, page_scores, s);
+    if (k_new) {
+        st = launch_append(*g, dtype, B, *cache, nullptr, seq_lens, 1, k_new, v_new, summaries, s);
+        if (st != RKV_OK) return st;
+    }
     if (!page_idx) {
         page_idx = (int32_t *)((char *)ws + align_up(select_ws_bytes(*g, B, cache->max_pages, k2)) +
                                align_up(attend_ws_bytes(*g, B, cache->page_size, k2)));
     }
-    hipStream_t s = (hipStream_t)stream;
     st = launch_select(*g, dtype, B, q, seq_lens, cache->page_size, cache->max_pages, summaries,
                        k1, k2, chan_idx, page_idx, page_scores, ws, s);
     if (st != RKV_OK) return st;
     char *base = (char *)ws + align_up(select_ws_bytes(*g, B, cache->max_pages, k2));
     return launch_attend(*g, dtype, B, q, *cache, seq_lens, page_idx, k2, scale, out, base, s);
+}
+
+int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
+                   const rkv_paged_cache *cache, const int32_t *seq_lens, const void *summaries,
+                   int32_t k1, int32_t k2, float scale, float *out, int32_t *chan_idx,
+                   int32_t *page_idx, float *page_scores, void *ws, size_t ws_bytes,
+                   void *stream) {
+    return rkv_decode_step(g, dtype, B, q, nullptr, nullptr, cache, seq_lens, (void *)summaries,
+                           k1, k2, scale, out, chan_idx, page_idx, page_scores, ws, ws_bytes,
+                           stream);
 }
 
 }  // extern "C"

@@ -68,6 +68,16 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
 }
 
 // ---- block-wide helpers ---------------------------------------------------
+// Barrier that orders LDS only: unlike __syncthreads() it does not wait for
+// the block's outstanding global stores, so a block that has written optional
+// outputs or cache rows can keep going.  Use __syncthreads() whenever threads
+// exchange data through global memory.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Exclusive prefix count of `flag` over the threads of the block, in thread
 // order.  `wave_tot` is LDS scratch of NW ints.  All threads must call it.
 template <int NW>
@@ -78,7 +88,7 @@ __device__ __forceinline__ int block_excl_count(bool flag, int *wave_tot, int &t
     const uint64_t below = lane ? (b & (~0ull >> (64 - lane))) : 0ull;
     const int in_wave = __popcll(below);
     if (lane == 0) wave_tot[w] = __popcll(b);
-    __syncthreads();
+    lds_barrier();
     int off = 0, tot = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
@@ -86,7 +96,7 @@ __device__ __forceinline__ int block_excl_count(bool flag, int *wave_tot, int &t
         off += (i < w) ? t : 0;
         tot += t;
     }
-    __syncthreads();
+    lds_barrier();
     total = tot;
     return off + in_wave;
 }
@@ -102,12 +112,12 @@ __device__ void block_topk_threshold(Load load, int n, int K, uint32_t *hist, in
     int remaining = K;
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int i = threadIdx.x; i < 256; i += BLOCK) hist[i] = 0u;
-        __syncthreads();
+        lds_barrier();
         for (int i = threadIdx.x; i < n; i += BLOCK) {
             const uint32_t u = load(i);
             if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
         }
-        __syncthreads();
+        lds_barrier();
         if (threadIdx.x < kWave) {
             const int lane = threadIdx.x;
             // lane owns bins 255-4*lane .. 252-4*lane (descending order)
@@ -138,12 +148,12 @@ __device__ void block_topk_threshold(Load load, int n, int K, uint32_t *hist, in
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         const uint32_t digit = (uint32_t)sh[0];
         remaining -= sh[1];
         prefix |= digit << shift;
         mask |= 255u << shift;
-        __syncthreads();
+        lds_barrier();
     }
     thr = prefix;
     take_eq = remaining;
@@ -183,6 +193,7 @@ inline int launch_status() {
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
 // ---- internal launchers (one translation unit each) -----------------------
+// n_old == nullptr appends exactly one row per sequence, ending at n_new.
 int launch_append(const rkv_gqa &g, int dtype, int B, const rkv_paged_cache &c,
                   const int32_t *n_old, const int32_t *n_new, int max_new_rows,
                   const void *k_src, const void *v_src, void *summaries, hipStream_t s);
@@ -201,12 +212,21 @@ int launch_select(const rkv_gqa &g, int dtype, int B, const void *q, const int32
 struct AttendPlan {
     int pages_per_block;
     int n_splits;
+    int waves;    // waves per block
+    int variant;  // kernel variant (waves, loads per iteration, pipelining)
 };
 AttendPlan plan_attend(const rkv_gqa &g, int B, int P, int k2);
 size_t attend_ws_bytes(const rkv_gqa &g, int B, int P, int k2);
 int launch_attend(const rkv_gqa &g, int dtype, int B, const void *q,
                   const rkv_paged_cache &c, const int32_t *seq_lens, const int32_t *page_idx,
                   int k2, float scale, float *out, void *ws, hipStream_t s);
+
+bool fused_decode_ok(const rkv_gqa &g, int B, int P, int max_pages, int k2);
+int launch_decode_fused(const rkv_gqa &g, int dtype, int B, const void *q, const void *k_new,
+                        const void *v_new, const rkv_paged_cache &c, const int32_t *seq_lens,
+                        void *summaries, int k1, int k2, float scale, float *out,
+                        int32_t *chan_idx, int32_t *page_idx, float *page_scores,
+                        hipStream_t s);
 
 struct EvictSeq {
     int32_t L[RKV_MAX_EVICT_BATCH];

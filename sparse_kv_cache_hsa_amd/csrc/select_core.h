@@ -1,0 +1,323 @@
+// select_core.h -- device building blocks of HSA selection, shared by the
+// selection kernel and the fused decode kernel so both compute identical bits.
+//
+// "RocketKV-adapted -- Two-Stage Compression", section "Where it sits": the
+// score is approximated with SparQ-style top-magnitude channels (head
+// dimension) and Quest-style page max/min summaries (sequence dimension),
+// giving a per-page bound; "Adaptation notes": k2 whole pages are kept.
+//   channel rank : a[c] = sum_j |q_j[c]| (fp32, heads ascending, from +0),
+//                  the k1 largest (ties to the lower channel), ascending;
+//   page bound   : s_j(p) = sum_{c in I1 asc} max(q_j[c]*Kmax[p][c],
+//                  q_j[c]*Kmin[p][c]); S(p) = sum_{j asc} s_j(p), all plain
+//                  fp32 operations (this library is built without
+//                  multiply-add contraction);
+//   page top-k   : the min(k2, NP) largest S (ties to the lower page),
+//                  reported in ascending page order.
+// Rankings use 64-bit composite keys (order-preserving 32-bit score key in
+// the high word, complemented index in the low word), so "larger key" is
+// exactly "higher score, then lower index" and every comparison is one
+// unsigned 64-bit compare.
+#pragma once
+
+#include "rkv_internal.h"
+
+namespace rkv {
+
+__device__ __forceinline__ uint64_t composite_key(uint32_t key, int index) {
+    return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)index);
+}
+
+// q rows of the G query heads of KV head (b, h) into LDS as fp32.
+template <typename T, int D, int G, int BLOCK>
+__device__ __forceinline__ void load_group_q(const T *q, int64_t bh, float (*qs)[D]) {
+    for (int i = threadIdx.x; i < G * D; i += BLOCK) qs[i / D][i % D] = Elem<T>::ld(q, bh * G * D + i);
+}
+
+// Rank count for n <= BLOCK composite keys comp_s[0..n) (LDS): every key is
+// compared with every other, the comparisons of one key spread over
+// BLOCK/n threads; then emit(pos, i) for the K largest, i ascending.
+// cnt_s is LDS scratch of n ints.  All threads must call it; comp_s must be
+// visible to the block.
+template <int BLOCK, typename Emit>
+__device__ void rank_topk(const uint64_t *comp_s, int n, int K, int *cnt_s, int *wave_tot,
+                          Emit emit) {
+    constexpr int NW = BLOCK / kWave;
+    const int tid = threadIdx.x;
+    const int npad = (n + kWave - 1) / kWave * kWave;
+    int parts = npad > 0 ? BLOCK / npad : 1;
+    parts = parts < 1 ? 1 : (parts > 8 ? 8 : parts);
+    if (parts > 1) {
+        for (int i = tid; i < n; i += BLOCK) cnt_s[i] = 0;
+        lds_barrier();
+    }
+    const int i = tid % npad, part = tid / npad;
+    if (part < parts && i < n) {
+        const uint64_t key = comp_s[i];
+        const int chunk = (n + parts - 1) / parts;
+        const int j0 = part * chunk, j1 = min(n, j0 + chunk);
+        int c = 0;
+#pragma unroll 8
+        for (int j = j0; j < j1; ++j) c += comp_s[j] > key;
+        if (parts > 1) atomicAdd(&cnt_s[i], c);
+        else cnt_s[i] = c;
+    }
+    lds_barrier();
+    const bool sel = tid < n && cnt_s[tid] < K;
+    int tot;
+    const int pos = block_excl_count<NW>(sel, wave_tot, tot);
+    if (sel) emit(pos, tid);
+}
+
+// Channel ranking.  qs must be visible to the block.  On return ch_s[0..k1)
+// holds the chosen channels in ascending order and qsel[j][i] = qs[j][ch_s[i]]
+// (both visible to the block).  comp_s: LDS scratch of D uint64, cnt_s of D
+// ints.  Requires D <= BLOCK.
+template <int D, int G, int BLOCK>
+__device__ __forceinline__ void rank_channels(const float (*qs)[D], int k1, uint64_t *comp_s,
+                                              int *cnt_s, int *ch_s, float (*qsel)[D],
+                                              int *wave_tot) {
+    const int tid = threadIdx.x;
+    if (tid < D) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < G; ++j) acc = acc + fabsf(qs[j][tid]);
+        // acc >= +0, so its bits order like its value
+        comp_s[tid] = composite_key(__float_as_uint(acc), tid);
+    }
+    lds_barrier();
+    rank_topk<BLOCK>(comp_s, D, k1, cnt_s, wave_tot, [&](int o, int c) { ch_s[o] = c; });
+    lds_barrier();
+    for (int t = tid; t < G * k1; t += BLOCK) qsel[t / k1][t % k1] = qs[t / k1][ch_s[t % k1]];
+    lds_barrier();
+}
+
+// Page bound S(p).  smax/smin point at channel 0 of the (b, h) summaries;
+// channel c of page p sits at c * max_pages + p.  The summary pairs of a
+// batch of up to 32 channels are loaded before use, so one memory round trip
+// serves the batch.
+template <typename T, int D, int G>
+__device__ __forceinline__ float page_bound(const T *smax, const T *smin, int max_pages, int p,
+                                            const int *ch_s, int k1, const float (*qsel)[D]) {
+    constexpr int CB = 32;
+    float s[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) s[j] = 0.0f;
+    for (int i0 = 0; i0 < k1; i0 += CB) {
+        float hi_v[CB], lo_v[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const int i = i0 + u;
+            const int c = __builtin_amdgcn_readfirstlane(ch_s[i < k1 ? i : 0]);
+            hi_v[u] = Elem<T>::ld(smax, (int64_t)c * max_pages + p);
+            lo_v[u] = Elem<T>::ld(smin, (int64_t)c * max_pages + p);
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            if (i0 + u < k1) {
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    const float qc = qsel[j][i0 + u];
+                    const float hi = qc * hi_v[u];
+                    const float lo = qc * lo_v[u];
+                    s[j] = s[j] + (hi > lo ? hi : lo);
+                }
+            }
+        }
+    }
+    float tot = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) tot = tot + s[j];
+    return tot;
+}
+
+// Page bound of a page whose summary is held in LDS (ovr_hi/ovr_lo indexed
+// by channel), same arithmetic and order as page_bound.
+template <typename T, int D, int G>
+__device__ __forceinline__ float page_bound_ovr(const int *ch_s, int k1, const float (*qsel)[D],
+                                                const T *ovr_hi, const T *ovr_lo) {
+    float s[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) s[j] = 0.0f;
+    for (int i = 0; i < k1; ++i) {
+        const float hv = Elem<T>::ld(ovr_hi, ch_s[i]);
+        const float lv = Elem<T>::ld(ovr_lo, ch_s[i]);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float qc = qsel[j][i];
+            const float hi = qc * hv;
+            const float lo = qc * lv;
+            s[j] = s[j] + (hi > lo ? hi : lo);
+        }
+    }
+    float tot = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) tot = tot + s[j];
+    return tot;
+}
+
+// Top-K of comp_s[0..n) (composite keys, LDS) with emit(pos, i), i
+// ascending.  Up to BLOCK keys use the rank count, more a 4-pass radix
+// select on the score word (ties then resolve to the lower index).  All
+// threads must call it; comp_s must be visible to the block.
+template <int BLOCK, typename Emit>
+__device__ void topk_ascending(const uint64_t *comp_s, int n, int K, int *cnt_s, uint32_t *hist,
+                               int *sh, int *wave_tot, Emit emit) {
+    if (K <= 0) return;
+    if (n <= BLOCK) {
+        rank_topk<BLOCK>(comp_s, n, K, cnt_s, wave_tot, emit);
+        return;
+    }
+    uint32_t thr;
+    int take_eq;
+    auto load = [&](int i) { return (uint32_t)(comp_s[i] >> 32); };
+    block_topk_threshold<BLOCK>(load, n, K, hist, sh, thr, take_eq);
+    block_topk_emit<BLOCK>(load, n, thr, take_eq, wave_tot, emit);
+}
+
+
+// ---- staged page bounds ------------------------------------------------------
+// Copies the summaries of the k1 chosen channels for pages [p0, p0 + n) into
+// LDS as stage[kind][i][p - p0] (kind 0 = max, 1 = min) with row stride npad,
+// using the direct global-to-LDS loads of gfx950: no register round trip, so
+// every load of the block is in flight at once and one wait ends the copy.
+// The stage is a contiguous run of E-element chunks (E = 8 bf16 / 4 fp32 when
+// every row is 16-byte aligned, else 1), chunk t at element t * E, which is
+// the per-lane destination pattern of these loads: a wave's 64 consecutive
+// chunks land in 64 consecutive slots.  Returns npad (n rounded up to E).
+// The caller synchronises the block afterwards (lds_barrier).
+template <typename T, int E, int BLOCK>
+__device__ __forceinline__ void stage_rows(const T *smax, const T *smin, int max_pages, int p0,
+                                           int nv, const int *ch_s, int k1, T *stage) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int total = 2 * k1 * nv;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int base = threadIdx.x - lane; base < total; base += BLOCK) {
+        const int t = base + lane;
+        if (t < total) {
+            const int row = t / nv, vi = t - row * nv;
+            const int kind = row / k1, i = row - kind * k1;
+            const T *src = (kind ? smin : smax) + (int64_t)ch_s[i] * max_pages + p0 + vi * E;
+            // The byte count must be an int constant: a size_t expression
+            // crashes this compiler's instruction selection.
+            __builtin_amdgcn_global_load_lds(src, (lds_void *)(stage + (int64_t)base * E),
+                                             (int)(E * sizeof(T)), 0, 0);
+        }
+    }
+}
+
+template <typename T, int BLOCK>
+__device__ __forceinline__ int stage_summaries(const T *smax, const T *smin, int max_pages, int p0,
+                                               int n, const int *ch_s, int k1, T *stage) {
+    constexpr int V = 16 / (int)sizeof(T);
+    const bool vec = (max_pages % V) == 0 && (p0 % V) == 0 &&
+                     (((uintptr_t)smax) & 15u) == 0 && (((uintptr_t)smin) & 15u) == 0;
+    int npad;
+    if (vec) {
+        const int nv = (n + V - 1) / V;
+        stage_rows<T, V, BLOCK>(smax, smin, max_pages, p0, nv, ch_s, k1, stage);
+        npad = nv * V;
+    } else if constexpr (sizeof(T) == 4) {
+        stage_rows<T, 1, BLOCK>(smax, smin, max_pages, p0, n, ch_s, k1, stage);
+        npad = n;
+    } else {
+        // Sub-dword direct loads fill a dword per lane, which does not match
+        // this packing; copy through registers instead.
+        for (int t = threadIdx.x; t < 2 * k1 * n; t += BLOCK) {
+            const int row = t / n, pi = t - row * n;
+            const int kind = row / k1, i = row - kind * k1;
+            stage[t] = (kind ? smin : smax)[(int64_t)ch_s[i] * max_pages + p0 + pi];
+        }
+        npad = n;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+    return npad;
+}
+
+// Page bound S(p) from staged summaries (same arithmetic and order as
+// page_bound).
+template <typename T, int D, int G>
+__device__ __forceinline__ float staged_bound(const T *stage, int npad, int p, int k1,
+                                              const float (*qsel)[D]) {
+    float s[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) s[j] = 0.0f;
+    const T *hi_row = stage + p;
+    const T *lo_row = stage + (int64_t)k1 * npad + p;
+    for (int i = 0; i < k1; ++i) {
+        const float hv = Elem<T>::ld(hi_row, (int64_t)i * npad);
+        const float lv = Elem<T>::ld(lo_row, (int64_t)i * npad);
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float qc = qsel[j][i];
+            const float hi = qc * hv;
+            const float lo = qc * lv;
+            s[j] = s[j] + (hi > lo ? hi : lo);
+        }
+    }
+    float tot = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) tot = tot + s[j];
+    return tot;
+}
+
+// ---- top-k by per-wave sorting ----------------------------------------------
+// 64-bit lane shuffle.
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Sorts the 64 keys of a wave in descending order (lane i gets the i-th
+// largest) with a bitonic network of register shuffles.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t other = shfl_xor64(key, j);
+            const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
+            const uint64_t mx = key > other ? key : other;
+            const uint64_t mn = key > other ? other : key;
+            key = keep_max ? mx : mn;
+        }
+    }
+    return key;
+}
+
+// Top-K of n <= BLOCK composite keys, key i held by thread i (threads >= n
+// pass 0, below every real key).  Every wave sorts its keys into LDS
+// (sorted_s: BLOCK uint64); the rank of a key is the number of larger keys in
+// all sorted lists, found by binary search; emit(pos, i) for the K largest,
+// i ascending.  All threads must call it.
+template <int BLOCK, typename Emit>
+__device__ void sort_topk(uint64_t key, int n, int K, uint64_t *sorted_s, int *wave_tot,
+                          Emit emit) {
+    constexpr int NW = BLOCK / kWave;
+    const int tid = threadIdx.x, w = tid / kWave;
+    const int nw = (n + kWave - 1) / kWave;  // waves holding real keys
+    if (w < nw) sorted_s[tid] = wave_sort_desc(key);
+    lds_barrier();
+    bool sel = false;
+    if (tid < n) {
+        int rank = 0;
+        for (int l = 0; l < nw; ++l) {
+            // number of entries > key in the descending list l
+            const uint64_t *list = sorted_s + l * kWave;
+            int lo = 0, hi = kWave;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (list[mid] > key) lo = mid + 1;
+                else hi = mid;
+            }
+            rank += lo;
+        }
+        sel = rank < K;
+    }
+    int tot;
+    const int pos = block_excl_count<NW>(sel, wave_tot, tot);
+    if (sel) emit(pos, tid);
+}
+
+}  // namespace rkv

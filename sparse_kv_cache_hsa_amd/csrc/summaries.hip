@@ -22,7 +22,8 @@ append_kernel(int Hkv, int P, int max_pages, int64_t num_blocks, const int32_t *
               const T *k_src, const T *v_src, T *summ) {
     const int b = blockIdx.z, h = blockIdx.y, c = threadIdx.x;
     const int64_t cap = (int64_t)max_pages * P;
-    const int64_t o = min<int64_t>(max<int64_t>(n_old[b], 0), cap);
+    const int64_t o_in = n_old ? (int64_t)n_old[b] : (int64_t)n_new[b] - 1;
+    const int64_t o = min<int64_t>(max<int64_t>(o_in, 0), cap);
     int64_t e = min<int64_t>(max<int64_t>(n_new[b], 0), cap);
     e = min<int64_t>(e, o + max_new);
     if (e <= o) return;

@@ -33,6 +33,7 @@ EXPORTED = (
     "rkv_status_string", "rkv_build_id", "rkv_split_ratio",
     "rkv_prefill_evict_workspace_bytes", "rkv_prefill_evict", "rkv_append_summaries",
     "rkv_hsa_workspace_bytes", "rkv_hsa_select", "rkv_hsa_attend", "rkv_hsa_decode",
+    "rkv_decode_step",
 )
 
 
@@ -94,6 +95,9 @@ def load_library(path: str | None = None, check_build_id: bool = True):
         lib.rkv_hsa_decode.argtypes = [G, i32, i32, vp, C, vp, vp, i32, i32, f32, vp, vp, vp,
                                        vp, vp, sz, vp]
         lib.rkv_hsa_decode.restype = ctypes.c_int
+        lib.rkv_decode_step.argtypes = [G, i32, i32, vp, vp, vp, C, vp, vp, i32, i32, f32, vp,
+                                        vp, vp, vp, vp, sz, vp]
+        lib.rkv_decode_step.restype = ctypes.c_int
         if check_build_id:
             built = lib.rkv_build_id().decode()
             want = _build.source_hash()
@@ -168,6 +172,17 @@ class PagedCache:
     def row_slice(self, b0: int, b1: int) -> "PagedCache":
         """The same pools with the page-table rows of sequences [b0, b1)."""
         return PagedCache(self.k_pool, self.v_pool, self.page_table[b0:b1])
+
+
+def fused_path(g: rkv_gqa, B: int, page_size: int, max_pages: int, k2: int) -> bool:
+    """Whether rkv_decode_step runs as one fused kernel for these shapes (the
+    rule documented in include/rkv.h; RKV_FUSED=0/1 overrides it)."""
+    env = os.environ.get("RKV_FUSED", "")
+    if g.group > 4 or g.group * g.head_dim > 512 or max_pages > 2048 or k2 * page_size > 2048:
+        return False
+    if env in ("0", "1"):
+        return env == "1"
+    return B * g.n_kv_heads >= 192
 
 
 # ---- entry points (same names as the C ABI) ---------------------------------
@@ -300,3 +315,29 @@ def rkv_hsa_decode(g: rkv_gqa, q: torch.Tensor, cache: PagedCache, seq_lens: tor
         seq_lens.data_ptr(), summaries.data_ptr(), int(k1), int(k2), float(scale),
         out.data_ptr(), _ptr(chan_idx), _ptr(page_idx), _ptr(page_scores), ws.data_ptr(),
         ws.numel(), _stream()))
+
+
+def rkv_decode_step(g: rkv_gqa, q: torch.Tensor, k_new: torch.Tensor | None,
+                    v_new: torch.Tensor | None, cache: PagedCache, seq_lens: torch.Tensor,
+                    summaries: torch.Tensor, k1: int, k2: int, scale: float, out: torch.Tensor,
+                    ws: torch.Tensor, chan_idx: torch.Tensor | None = None,
+                    page_idx: torch.Tensor | None = None,
+                    page_scores: torch.Tensor | None = None) -> None:
+    """Append the new token (row seq_lens-1 from k_new/v_new [B, Hkv, d]) and
+    run HSA decode, in one call per layer."""
+    _need(q, "q", cache.k_pool.dtype)
+    _need(k_new, "k_new", q.dtype, optional=True)
+    _need(v_new, "v_new", q.dtype, optional=True)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(summaries, "summaries", q.dtype)
+    _need(out, "out", torch.float32)
+    _need(chan_idx, "chan_idx", torch.int32, optional=True)
+    _need(page_idx, "page_idx", torch.int32, optional=True)
+    _need(page_scores, "page_scores", torch.float32, optional=True)
+    _need(ws, "ws")
+    cs = cache.c_struct()
+    _check("rkv_decode_step", load_library().rkv_decode_step(
+        ctypes.byref(g), _dtype_code(q), int(q.shape[0]), q.data_ptr(), _ptr(k_new),
+        _ptr(v_new), ctypes.byref(cs), seq_lens.data_ptr(), summaries.data_ptr(), int(k1),
+        int(k2), float(scale), out.data_ptr(), _ptr(chan_idx), _ptr(page_idx),
+        _ptr(page_scores), ws.data_ptr(), ws.numel(), _stream()))

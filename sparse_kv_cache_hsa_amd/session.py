@@ -32,7 +32,8 @@ class Session:
         turn_rows = wl.turns * (wl.turn_append + wl.decode_steps)
         self.capacity = [k + extra_rows + turn_rows for k in self.keep]
         pages = [math.ceil(c / self.P) for c in self.capacity]
-        self.max_pages = max(pages)
+        # a multiple of 8 keeps every summary row 16-byte aligned (wide loads)
+        self.max_pages = -(-max(pages) // 8) * 8
         table, self.num_blocks = synth.page_table(wl.seed, self.B, pages, self.max_pages)
         self.page_table = table.to(self.dev)
         shape = (self.num_blocks, self.Hkv, self.P, self.d)
@@ -111,7 +112,7 @@ class Session:
 
     # ---- decode ------------------------------------------------------------
     def make_inputs(self, steps: int, turn: int = 0):
-        """Per step and layer: new K/V rows [B, Hkv, 1, d], queries [B, Hq, d],
+        """Per step and layer: new K/V rows [B, Hkv, d], queries [B, Hq, d],
         and the row counts before/after the step."""
         pos0 = torch.tensor(self.positions(), dtype=torch.int64)
         rows0 = torch.tensor(self.rows, dtype=torch.int32)
@@ -120,22 +121,21 @@ class Session:
             per_layer = []
             for l in range(self.n_layers):
                 k, v, q = self.wl.decode_tokens(l, s, pos0 + s, turn=turn, device=self.dev)
-                per_layer.append((k[:, :, None].contiguous(), v[:, :, None].contiguous(), q))
+                per_layer.append((k, v, q))
             n_old = (rows0 + s).to(self.dev)
             n_new = (rows0 + s + 1).to(self.dev)
             inputs.append((per_layer, n_old, n_new))
         return inputs
 
-    def step(self, inp, attend_only_hook=None):
-        """One decode step over every layer (enqueue only)."""
-        per_layer, n_old, n_new = inp
+    def step(self, inp):
+        """One decode step over every layer (enqueue only): per layer, append
+        the token and run HSA decode in one library call."""
+        per_layer, _, n_new = inp
         for l in range(self.n_layers):
             k, v, q = per_layer[l]
-            rkv.rkv_append_summaries(self.g, self.caches[l], n_old, n_new, 1, self.summ[l],
-                                     k_src=k, v_src=v)
-            rkv.rkv_hsa_decode(self.g, q, self.caches[l], n_new, self.summ[l], self.wl.k1,
-                               self.wl.k2, self.scale, self.out, self.ws,
-                               page_idx=self.page_idx[l])
+            rkv.rkv_decode_step(self.g, q, k, v, self.caches[l], n_new, self.summ[l],
+                                self.wl.k1, self.wl.k2, self.scale, self.out, self.ws,
+                                page_idx=self.page_idx[l])
 
     def advance(self, steps: int):
         self.rows = [r + steps for r in self.rows]

@@ -37,7 +37,9 @@ DECODE_CASES = [
 ]
 
 
-def run_decode_case(case, seed, q_override=None, k_override=None):
+def run_decode_case(case, seed, q_override=None, k_override=None, mode="decode"):
+    """mode: "decode" (rkv_hsa_decode on a filled cache) or "step" (the cache
+    holds rows [0, n-1) and rkv_decode_step appends row n-1 itself)."""
     rkv = lib()
     dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages = case
     Lmax = max(max(lens), 1)
@@ -48,7 +50,13 @@ def run_decode_case(case, seed, q_override=None, k_override=None):
     pages = [min(max_pages, n_pages(n, P) + 1) for n in lens]
     cache, summ = make_cache(Hkv, d, P, max_pages, pages, dtype, seed)
     Kd, Vd, qd = K.cuda(), V.cuda(), q.cuda()
-    fill_cache(g, cache, summ, Kd, Vd, lens)
+    if mode == "step":
+        fill_cache(g, cache, summ, Kd, Vd, [max(n - 1, 0) for n in lens])
+        last = torch.tensor([max(n - 1, 0) for n in lens])
+        k_new = torch.stack([Kd[b, :, last[b]] for b in range(B)]).contiguous()
+        v_new = torch.stack([Vd[b, :, last[b]] for b in range(B)]).contiguous()
+    else:
+        fill_cache(g, cache, summ, Kd, Vd, lens)
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     out = torch.full((B, Hkv * G, d), float("nan"), device="cuda")
     chan = torch.full((B, Hkv, k1), -7, dtype=torch.int32, device="cuda")
@@ -56,8 +64,12 @@ def run_decode_case(case, seed, q_override=None, k_override=None):
     scores = torch.zeros((B, Hkv, max_pages), dtype=torch.float32, device="cuda")
     ws = rkv.hsa_workspace(g, B, P, max_pages, k1, k2, "cuda")
     scale = scale_for(d)
-    rkv.rkv_hsa_decode(g, qd, cache, seq, summ, k1, k2, scale, out, ws, chan_idx=chan,
-                       page_idx=pidx, page_scores=scores)
+    if mode == "step":
+        rkv.rkv_decode_step(g, qd, k_new, v_new, cache, seq, summ, k1, k2, scale, out, ws,
+                            chan_idx=chan, page_idx=pidx, page_scores=scores)
+    else:
+        rkv.rkv_hsa_decode(g, qd, cache, seq, summ, k1, k2, scale, out, ws, chan_idx=chan,
+                           page_idx=pidx, page_scores=scores)
     torch.cuda.synchronize()
     worst = 0.0
     for b in range(B):
@@ -82,9 +94,44 @@ def run_decode_case(case, seed, q_override=None, k_override=None):
     return worst, out
 
 
+@pytest.fixture(params=["auto", "fused", "split"])
+def path(request, monkeypatch):
+    """Which implementation rkv_hsa_decode / rkv_decode_step dispatch to."""
+    if request.param == "fused":
+        monkeypatch.setenv("RKV_FUSED", "1")
+    elif request.param == "split":
+        monkeypatch.setenv("RKV_FUSED", "0")
+    return request.param
+
+
+def fused_supported(case):
+    dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages = case
+    return G <= 4 and G * d <= 512 and max_pages <= 2048 and k2 * P <= 2048
+
+
 @pytest.mark.parametrize("ci", range(len(DECODE_CASES)))
-def test_decode_matches_oracle(ci):
-    run_decode_case(DECODE_CASES[ci], 1000 + ci)
+@pytest.mark.parametrize("mode", ["decode", "step"])
+def test_decode_matches_oracle(ci, mode, path):
+    case = DECODE_CASES[ci]
+    if path == "fused" and not fused_supported(case):
+        pytest.skip("shape outside the fused kernel's limits (dispatches to the split path)")
+    run_decode_case(case, 1000 + ci, mode=mode)
+
+
+# A batch large enough for the fused kernel by default (B * Hkv >= 192).
+BIG_CASE = (BF16, 24, 8, 4, 128, 16, 32, 64, [4000 + 37 * i for i in range(24)], 320)
+
+
+def test_decode_large_batch_default_path():
+    run_decode_case(BIG_CASE, 77, mode="step")
+
+
+def test_fused_and_split_select_identically(monkeypatch):
+    monkeypatch.setenv("RKV_FUSED", "1")
+    a = run_decode_case(BIG_CASE, 78, mode="step")[1].clone()
+    monkeypatch.setenv("RKV_FUSED", "0")
+    b = run_decode_case(BIG_CASE, 78, mode="step")[1]
+    assert (a - b).abs().max().item() < 1e-5
 
 
 def test_decode_ties_zero_query_and_identical_keys():
@@ -146,9 +193,11 @@ def test_append_in_chunks_matches_rebuild(dtype):
                        summ2.view(torch.int16 if dtype == BF16 else torch.int32))
 
 
-def test_tiny_workload_decode_loop():
+@pytest.mark.parametrize("fused", ["1", "0"])
+def test_tiny_workload_decode_loop(fused, monkeypatch):
     """The tiny fp32 workload end to end: 2,048 cached rows, 32 decode steps,
-    each appending its token through the library before HSA."""
+    each appending its token and decoding in one rkv_decode_step call."""
+    monkeypatch.setenv("RKV_FUSED", fused)
     rkv = lib()
     wl = workloads.TINY
     B, Hkv, G, d, P = wl.batch, wl.n_kv_heads, wl.group, wl.head_dim, wl.page_size
@@ -176,12 +225,9 @@ def test_tiny_workload_decode_loop():
     n = n0
     for step in range(wl.decode_steps):
         kt, vt, qt = wl.decode_tokens(0, step, torch.tensor([n]))
-        rkv.rkv_append_summaries(g, cache, torch.tensor([n], dtype=torch.int32, device="cuda"),
-                                 torch.tensor([n + 1], dtype=torch.int32, device="cuda"), 1, summ,
-                                 k_src=kt[:, :, None].cuda(), v_src=vt[:, :, None].cuda())
         seq = torch.tensor([n + 1], dtype=torch.int32, device="cuda")
-        rkv.rkv_hsa_decode(g, qt.cuda(), cache, seq, summ, wl.k1, wl.k2, scale, out, ws,
-                           chan_idx=chan, page_idx=pidx)
+        rkv.rkv_decode_step(g, qt.cuda(), kt.cuda(), vt.cuda(), cache, seq, summ, wl.k1, wl.k2,
+                            scale, out, ws, chan_idx=chan, page_idx=pidx)
         torch.cuda.synchronize()
         for h in range(Hkv):
             Ko[h][n], Vo[h][n] = kt[0, h].numpy(), vt[0, h].numpy()
