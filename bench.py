@@ -57,6 +57,21 @@ def step_bytes(sess, rows_now, per_head_rows):
     return (q + summaries + out + append) * sess.n_layers + sum(kv), kv[0] + q + out
 
 
+def counted_traffic(kernel: str, workload: str, build_id: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none for
+    this workload or it was taken on another build of the kernels."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("build_id") != build_id or rec.get("workload") != workload:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(wl, sess, budget_s: float):
     """The oracle's decode step (summary append + HSA) on the host cores, on a
     bounded sample: layer 0 of every sequence and KV head, caches of the same
@@ -111,6 +126,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="enqueue steps eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device to device 3 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path has no multi-GPU leg "
@@ -121,6 +138,15 @@ def main():
 
     from sparse_kv_cache_hsa_amd import rkv, workloads
     from sparse_kv_cache_hsa_amd.session import Session
+
+    if args.copy_probe > 0:
+        x = torch.ones(args.copy_probe << 20, dtype=torch.uint8, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_probe} MiB device to device 3 times")
+        return
 
     rkv.load_library()
     wl = workloads.ALL[args.workload]
@@ -187,17 +213,15 @@ def main():
     log(f"[bench] algorithmic bytes per step {step_b / 1e9:.3f} GB, attended rows per "
         f"(sequence, layer) {attended_seq_layer:.1f}")
 
-    # ---- dominant kernel, timed alone ---------------------------------------
-    # Fused path: a step is one decode_kernel launch per layer, and replaying
-    # the last step's graph is idempotent (same row, same values, same
-    # summaries), so per-launch time = replay time / (replays * layers).
+    # ---- dominant kernel ----------------------------------------------------
+    # Fused path: a step is one decode_kernel launch per layer on this stream,
+    # so the timed region itself gives the average launch duration.
     # Split path: the attention launches of every layer, captured alone.
     per_layer, _, n_new = inputs[W + K - 1]
     fused = rkv.fused_path(sess.g, sess.B, sess.P, sess.max_pages, wl.k2)
-    reps = 20
-    if fused and graphs:
-        kernel = "decode_kernel (append + select + attend, one launch per layer)"
-        gph = graphs[W + K - 1]
+    if fused:
+        kernel = "decode_kernel"
+        launch_us = ms_total * 1e3 / (K * sess.n_layers)
         bytes_launch = step_b / sess.n_layers
     else:
         kernel = "attend_kernel"
@@ -211,18 +235,21 @@ def main():
                 rkv.rkv_hsa_attend(sess.g, per_layer[l][2], sess.caches[l], n_new,
                                    sess.page_idx[l], wl.k2, sess.scale, sess.out, sess.ws)
         bytes_launch = attend_b0
-    gph.replay()
-    torch.cuda.synchronize()
-    k0, k1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    k0.record()
-    for _ in range(reps):
         gph.replay()
-    k1e.record()
-    torch.cuda.synchronize()
-    launch_us = k0.elapsed_time(k1e) * 1e3 / (reps * sess.n_layers)
+        torch.cuda.synchronize()
+        reps = 20
+        k0, k1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k0.record()
+        for _ in range(reps):
+            gph.replay()
+        k1e.record()
+        torch.cuda.synchronize()
+        launch_us = k0.elapsed_time(k1e) * 1e3 / (reps * sess.n_layers)
     kern_gbs = bytes_launch / (launch_us * 1e-6) / 1e9
+    traffic = counted_traffic(kernel, wl.name, rkv.load_library().rkv_build_id().decode())
     log(f"[bench] {kernel}: {launch_us:.2f} us/launch, {bytes_launch / 1e6:.2f} MB/launch -> "
-        f"{kern_gbs:.0f} GB/s")
+        f"{kern_gbs:.0f} GB/s; counted traffic "
+        f"{'n/a' if traffic is None else f'{traffic / 1e6:.2f} MB/launch'}")
 
     steps_per_s = 1e3 / ms_step
     result = {
@@ -252,7 +279,7 @@ def main():
                    "graph": not args.no_graph, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(kern_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(launch_us, 3),
+                     "traffic": traffic, "avg_launch_us": round(launch_us, 3),
                      "bytes_per_launch": int(bytes_launch)},
     }
     if not args.no_cpu_baseline:
