@@ -44,6 +44,11 @@ __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
 }
 
+template <int OFF>
+__device__ __forceinline__ float xor_lanes(float v) {
+    return __uint_as_float(lane_xor<OFF>(__float_as_uint(v)));
+}
+
 // Sum over the LPR consecutive lanes that share a row; every lane of the row
 // gets the same bits (each step adds a commutative pair).
 template <int LPR>
@@ -53,16 +58,10 @@ __device__ __forceinline__ float row_sum(float v) {
     v += dpp<kDppXor2>(v);
     if constexpr (LPR >= 8) v += dpp<kDppHalfMirror>(v);
     if constexpr (LPR >= 16) v += dpp<kDppMirror>(v);
-    if constexpr (LPR >= 32) v += __shfl_xor(v, 16, kWave);
+    if constexpr (LPR >= 32) v += xor_lanes<16>(v);
     return v;
 }
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                           __builtin_bit_cast(bf16x2_t, b), c, false);
-}
 
 template <typename T, int D, int G, int NW, int U, bool PIPE>
 struct AttendCore {
@@ -162,7 +161,7 @@ struct AttendCore {
             for (int e = 0; e < EPL; ++e) acc[j][e] *= corr;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                sc[u][j] = ok[u] ? exp2f(sc[u][j] - mn) : 0.0f;
+                sc[u][j] = ok[u] ? fast_exp2(sc[u][j] - mn) : 0.0f;
                 lj += sc[u][j];
             }
             l[j] = lj;
@@ -211,24 +210,29 @@ struct AttendCore {
 
     // Merges the row groups of each wave and stores the waves' states in LDS.
     // The caller synchronises the block before combine().
-    __device__ __forceinline__ void to_shared(Shared &sh) {
-#pragma unroll
-        for (int off = LPR; off < kWave; off <<= 1) {
+    template <int OFF>
+    __device__ __forceinline__ void merge_groups() {
+        if constexpr (OFF < kWave) {
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const float mo = __shfl_xor(m[j], off, kWave);
-                const float lo = __shfl_xor(l[j], off, kWave);
+                const float mo = xor_lanes<OFF>(m[j]);
+                const float lo = xor_lanes<OFF>(l[j]);
                 const float mn = fmaxf(m[j], mo);
                 const float c1 = exp2_diff(m[j], mn), c2 = exp2_diff(mo, mn);
                 l[j] = l[j] * c1 + lo * c2;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) {
-                    const float ao = __shfl_xor(acc[j][e], off, kWave);
+                    const float ao = xor_lanes<OFF>(acc[j][e]);
                     acc[j][e] = acc[j][e] * c1 + ao * c2;
                 }
                 m[j] = mn;
             }
+            merge_groups<OFF * 2>();
         }
+    }
+
+    __device__ __forceinline__ void to_shared(Shared &sh) {
+        merge_groups<LPR>();
         if (rsub == 0) {
 #pragma unroll
             for (int j = 0; j < G; ++j) {

@@ -18,6 +18,8 @@
 // and split-K attention kernels run in sequence.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "attend_core.h"
 #include "select_core.h"
 
@@ -53,6 +55,8 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     constexpr size_t kUnion = cmax(cmax(kStageBytes, kKeyBytes), cmax(kRowBytes, kCoreBytes));
     __shared__ float qs[G][D];
     __shared__ float qsel[G][D];
+    __shared__ __align__(16) float qpm_s[D * 2 * G];
+    constexpr bool kPacked = std::is_same<T, uint16_t>::value;
     __shared__ int ch_s[D];
     __shared__ T ovr_hi[D], ovr_lo[D];
     __shared__ int32_t sel_s[RKV_MAX_K2];
@@ -81,38 +85,49 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
 
     // 1. append row n-1 and fold it into its page summary (first of equal
     //    values kept: strict comparisons, as in a rebuild); keep the page's new
-    //    summary in LDS for this block's own scoring.  Meanwhile prefetch the
-    //    page table row and the queries.
+    //    summary in LDS for this block's own scoring.  Every load of this
+    //    phase (the new row, the old summary, the page table row, the
+    //    queries) is issued before the first store, so the phase costs one
+    //    memory round trip.
     const bool append = k_new != nullptr && n > 0;
     const int p_new = append ? (int)((n - 1) / P) : -1;
+    const int slot = append ? (int)(n - 1 - (int64_t)p_new * P) : 0;
+    const int64_t im = (int64_t)tid * max_pages + p_new;
+    T x{}, vx{}, omax{}, omin{};
+    int32_t blk_new = -1;
     if (append && tid < D) {
-        const int slot = (int)(n - 1 - (int64_t)p_new * P);
-        const int32_t blk = a.page_table[(int64_t)b * max_pages + p_new];
-        const T x = k_new[bh * D + tid];
-        const int64_t im = (int64_t)tid * max_pages + p_new;
+        blk_new = a.page_table[(int64_t)b * max_pages + p_new];
+        x = k_new[bh * D + tid];
+        vx = v_new[bh * D + tid];
+        if (slot != 0) {
+            omax = sm_max[im];
+            omin = sm_min[im];
+        }
+    }
+    for (int p = tid; p < NP; p += kBlock) blk_s[p] = a.page_table[(int64_t)b * max_pages + p];
+    load_group_q<T, D, G, kBlock>(q, bh, qs);
+    if (append && tid < D) {
         T nmax = x, nmin = x;
         if (slot != 0) {
-            const T omax = sm_max[im], omin = sm_min[im];
             const float fx = Elem<T>::ld(&x, 0);
             nmax = fx > Elem<T>::ld(&omax, 0) ? x : omax;
             nmin = fx < Elem<T>::ld(&omin, 0) ? x : omin;
         }
         ovr_hi[tid] = nmax;
         ovr_lo[tid] = nmin;
-        if (blk >= 0 && blk < a.num_blocks) {
-            const int64_t dst = (((int64_t)blk * a.Hkv + h) * P + slot) * D + tid;
+        if (blk_new >= 0 && blk_new < a.num_blocks) {
+            const int64_t dst = (((int64_t)blk_new * a.Hkv + h) * P + slot) * D + tid;
             k_pool[dst] = x;
-            v_pool[dst] = v_new[bh * D + tid];
+            v_pool[dst] = vx;
             sm_max[im] = nmax;
             sm_min[im] = nmin;
         }
     }
-    for (int p = tid; p < NP; p += kBlock) blk_s[p] = a.page_table[(int64_t)b * max_pages + p];
-    load_group_q<T, D, G, kBlock>(q, bh, qs);
     lds_barrier();
 
     // 2. channels
-    rank_channels<D, G, kBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot);
+    rank_channels<D, G, kBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot,
+                                kPacked ? qpm_s : nullptr);
     if (a.chan_out && tid < k1) a.chan_out[bh * k1 + tid] = ch_s[tid];
 
     // 3-4. page bounds and page top-k2.  The summaries of the chosen channels
@@ -137,7 +152,11 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         lds_barrier();
         uint64_t key = 0;
         if (tid < NP) {
-            const float sc = staged_bound<T, D, G>(stage, npad, tid, k1, qsel);
+            float sc;
+            if constexpr (kPacked)
+                sc = staged_bound_exact<G>((const uint16_t *)stage, npad, tid, k1, qpm_s);
+            else
+                sc = staged_bound<T, D, G>(stage, npad, tid, k1, qsel);
             key = composite_key(ordered_key(sc), tid);
             if (a.score_out) a.score_out[bh * max_pages + tid] = sc;
         }

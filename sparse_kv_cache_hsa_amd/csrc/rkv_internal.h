@@ -180,9 +180,40 @@ __device__ void block_topk_emit(Load load, int n, uint32_t thr, int take_eq, int
     }
 }
 
+// 2^x with the hardware exponential (about 1 ulp; results below the
+// smallest normal may flush to zero, which only drops softmax weights under
+// 2^-126).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane (lane ^ OFF) of a 64-lane wave: DPP quad permutes for 1 and
+// 2, the lane swizzle within 32-lane halves for 4 to 16, and a permute
+// across the halves for 32.
+template <int OFF>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+    static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "offset");
+    if constexpr (OFF == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, true);
+    } else if constexpr (OFF == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, true);
+    } else if constexpr (OFF == 32) {
+        return (uint32_t)__shfl_xor((int)v, 32, kWave);
+    } else {
+        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (OFF << 10) | 0x1F);
+    }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.lo*b.lo + a.hi*b.hi + c for bf16 pairs a, b (products of bf16 values are
+// exact in fp32; fp32 accumulation).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 __device__ __forceinline__ float exp2_diff(float a, float b) {
     // exp2(a - b) with exp2(-inf - x) = 0, also when both are -inf.
-    return (a == -INFINITY) ? 0.0f : exp2f(a - b);
+    return (a == -INFINITY) ? 0.0f : fast_exp2(a - b);
 }
 
 // ---- launch helpers ------------------------------------------------------

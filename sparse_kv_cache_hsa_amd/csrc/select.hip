@@ -13,6 +13,8 @@
 //                   position order equals the page order for tie-breaking.
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "select_core.h"
 
 namespace rkv {
@@ -36,6 +38,8 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
     constexpr int NW = kSelBlock / kWave;
     __shared__ float qs[G][D];
     __shared__ float qsel[G][D];
+    __shared__ __align__(16) float qpm_s[D * 2 * G];
+    constexpr bool kPacked = std::is_same<T, uint16_t>::value;
     __shared__ int ch_s[D];
     __shared__ uint64_t comp_s[kMaxChunk];
     __shared__ __align__(16) T stage[kStageElems];
@@ -53,7 +57,8 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
 
     load_group_q<T, D, G, kSelBlock>(q, bh, qs);
     lds_barrier();
-    rank_channels<D, G, kSelBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot);
+    rank_channels<D, G, kSelBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot,
+                                       kPacked ? qpm_s : nullptr);
     if (a.chan_out && ck == 0 && tid < k1) a.chan_out[bh * k1 + tid] = ch_s[tid];
 
     const int p0 = ck * a.chunk;
@@ -66,7 +71,11 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
                                                        stage);
         lds_barrier();
         for (int pi = tid; pi < cnt; pi += kSelBlock) {
-            const float s = staged_bound<T, D, G>(stage, npad, pi, k1, qsel);
+            float s;
+            if constexpr (kPacked)
+                s = staged_bound_exact<G>((const uint16_t *)stage, npad, pi, k1, qpm_s);
+            else
+                s = staged_bound<T, D, G>(stage, npad, pi, k1, qsel);
             comp_s[pi] = composite_key(ordered_key(s), pi);
             if (a.score_out) a.score_out[bh * a.max_pages + p0 + pi] = s;
         }

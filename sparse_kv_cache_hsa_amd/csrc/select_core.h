@@ -70,12 +70,14 @@ __device__ void rank_topk(const uint64_t *comp_s, int n, int K, int *cnt_s, int 
 
 // Channel ranking.  qs must be visible to the block.  On return ch_s[0..k1)
 // holds the chosen channels in ascending order and qsel[j][i] = qs[j][ch_s[i]]
-// (both visible to the block).  comp_s: LDS scratch of D uint64, cnt_s of D
-// ints.  Requires D <= BLOCK.
+// (both visible to the block); if qpm is given (bf16 queries), also the
+// sign-split queries of staged_bound_exact, qpm[i * 2G + j] = max(q, 0) and
+// qpm[i * 2G + G + j] = min(q, 0) for q = qsel[j][i].  comp_s: LDS scratch
+// of D uint64, cnt_s of D ints.  Requires D <= BLOCK.
 template <int D, int G, int BLOCK>
 __device__ __forceinline__ void rank_channels(const float (*qs)[D], int k1, uint64_t *comp_s,
                                               int *cnt_s, int *ch_s, float (*qsel)[D],
-                                              int *wave_tot) {
+                                              int *wave_tot, float *qpm = nullptr) {
     const int tid = threadIdx.x;
     if (tid < D) {
         float acc = 0.0f;
@@ -87,7 +89,18 @@ __device__ __forceinline__ void rank_channels(const float (*qs)[D], int k1, uint
     lds_barrier();
     rank_topk<BLOCK>(comp_s, D, k1, cnt_s, wave_tot, [&](int o, int c) { ch_s[o] = c; });
     lds_barrier();
-    for (int t = tid; t < G * k1; t += BLOCK) qsel[t / k1][t % k1] = qs[t / k1][ch_s[t % k1]];
+    for (int t = tid; t < G * k1; t += BLOCK) {
+        const int j = t / k1, i = t % k1;
+        const float qv = qs[j][ch_s[i]];
+        qsel[j][i] = qv;
+        if (qpm) {
+            // by sign bit, so -0 goes to the Kmin side (both sides give a
+            // zero product there)
+            const bool neg = __float_as_uint(qv) >> 31;
+            qpm[i * 2 * G + j] = neg ? 0.0f : qv;
+            qpm[i * 2 * G + G + j] = neg ? qv : 0.0f;
+        }
+    }
     lds_barrier();
 }
 
@@ -260,37 +273,83 @@ __device__ __forceinline__ float staged_bound(const T *stage, int npad, int p, i
     return tot;
 }
 
+// bf16 page bound from staged summaries with fused multiply-adds.  For bf16
+// q and K every product q*K is exact in fp32, so fma(q, K, s) is s + q*K
+// rounded once, exactly the plain s + fl(q*K).  max(q*Kmax, q*Kmin) is q*Kmax
+// when q >= 0 and q*Kmin when q < 0; with q+ = max(q, 0) and q- = min(q, 0)
+// the two updates s = fma(q+, Kmax, s), s = fma(q-, Kmin, s) add that term
+// and a zero product (which leaves a sum that starts at +0 unchanged), so
+// S(p) has the same bits as staged_bound.
+template <int G>
+__device__ __forceinline__ float staged_bound_exact(const uint16_t *stage, int npad, int p, int k1,
+                                                    const float *qpm) {
+    float s[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) s[j] = 0.0f;
+    const uint16_t *hi_row = stage + p;
+    const uint16_t *lo_row = stage + (int64_t)k1 * npad + p;
+    for (int i = 0; i < k1; ++i) {
+        const float hv = __uint_as_float((uint32_t)hi_row[(int64_t)i * npad] << 16);
+        const float lv = __uint_as_float((uint32_t)lo_row[(int64_t)i * npad] << 16);
+        const float *qi = qpm + i * 2 * G;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            s[j] = __builtin_fmaf(qi[j], hv, s[j]);
+            s[j] = __builtin_fmaf(qi[G + j], lv, s[j]);
+        }
+    }
+    float tot = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) tot = tot + s[j];
+    return tot;
+}
+
 // ---- top-k by per-wave sorting ----------------------------------------------
-// 64-bit lane shuffle.
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+template <int J>
+__device__ __forceinline__ uint64_t key_xor(uint64_t v) {
+    const uint32_t lo = lane_xor<J>((uint32_t)v);
+    const uint32_t hi = lane_xor<J>((uint32_t)(v >> 32));
     return ((uint64_t)hi << 32) | lo;
 }
 
+// One compare-exchange stage of the bitonic network (merge size K, distance
+// J): the lane keeps the larger key when its position in the K-block and its
+// J-bit agree, so the wave ends sorted in descending order.
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_stage(uint64_t key, int lane) {
+    const uint64_t other = key_xor<J>(key);
+    const bool keep_max = ((lane & K) == 0) == ((lane & J) == 0);
+    const bool take = keep_max ? (other > key) : (other < key);
+    return take ? other : key;
+}
+
+template <int K, int J>
+__device__ __forceinline__ uint64_t bitonic_merge(uint64_t key, int lane) {
+    key = bitonic_stage<K, J>(key, lane);
+    if constexpr (J > 1) key = bitonic_merge<K, J / 2>(key, lane);
+    return key;
+}
+
 // Sorts the 64 keys of a wave in descending order (lane i gets the i-th
-// largest) with a bitonic network of register shuffles.
+// largest).  Distances 1 and 2 move through DPP, 4 to 16 through the lane
+// swizzle, 32 through a permute.
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
     const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint64_t other = shfl_xor64(key, j);
-            const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
-            const uint64_t mx = key > other ? key : other;
-            const uint64_t mn = key > other ? other : key;
-            key = keep_max ? mx : mn;
-        }
-    }
+    key = bitonic_merge<2, 1>(key, lane);
+    key = bitonic_merge<4, 2>(key, lane);
+    key = bitonic_merge<8, 4>(key, lane);
+    key = bitonic_merge<16, 8>(key, lane);
+    key = bitonic_merge<32, 16>(key, lane);
+    key = bitonic_merge<64, 32>(key, lane);
     return key;
 }
 
 // Top-K of n <= BLOCK composite keys, key i held by thread i (threads >= n
 // pass 0, below every real key).  Every wave sorts its keys into LDS
 // (sorted_s: BLOCK uint64); the rank of a key is the number of larger keys in
-// all sorted lists, found by binary search; emit(pos, i) for the K largest,
-// i ascending.  All threads must call it.
+// all sorted lists, found by binary searches that advance over every list in
+// the same step; emit(pos, i) for the K largest, i ascending.  All threads
+// must call it.
 template <int BLOCK, typename Emit>
 __device__ void sort_topk(uint64_t key, int n, int K, uint64_t *sorted_s, int *wave_tot,
                           Emit emit) {
@@ -301,18 +360,20 @@ __device__ void sort_topk(uint64_t key, int n, int K, uint64_t *sorted_s, int *w
     lds_barrier();
     bool sel = false;
     if (tid < n) {
-        int rank = 0;
-        for (int l = 0; l < nw; ++l) {
-            // number of entries > key in the descending list l
-            const uint64_t *list = sorted_s + l * kWave;
-            int lo = 0, hi = kWave;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (list[mid] > key) lo = mid + 1;
-                else hi = mid;
-            }
-            rank += lo;
+        // c[l] = number of entries > key in the descending list l
+        int c[NW];
+#pragma unroll
+        for (int l = 0; l < NW; ++l) c[l] = 0;
+#pragma unroll
+        for (int step = kWave / 2; step > 0; step >>= 1) {
+#pragma unroll
+            for (int l = 0; l < NW; ++l)
+                if (l < nw && sorted_s[l * kWave + c[l] + step - 1] > key) c[l] += step;
         }
+        int rank = 0;
+#pragma unroll
+        for (int l = 0; l < NW; ++l)
+            if (l < nw) rank += c[l] + (c[l] == kWave - 1 && sorted_s[l * kWave + kWave - 1] > key);
         sel = rank < K;
     }
     int tot;
