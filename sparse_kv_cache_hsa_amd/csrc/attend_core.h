@@ -58,10 +58,22 @@ __device__ __forceinline__ float row_sum(float v) {
     v += dpp<kDppXor2>(v);
     if constexpr (LPR >= 8) v += dpp<kDppHalfMirror>(v);
     if constexpr (LPR >= 16) v += dpp<kDppMirror>(v);
-    if constexpr (LPR >= 32) v += xor_lanes<16>(v);
+    if constexpr (LPR >= 32) v = pair_sum<16>(v);
     return v;
 }
 
+
+// Maximum over the row groups of a wave (every lane of a row group holds
+// the same value); every lane gets the result.
+template <int LPR>
+__device__ __forceinline__ float rows_max(float v) {
+    if constexpr (LPR < kWave) {
+        v = pair_max<LPR>(v);
+        return rows_max<LPR * 2>(v);
+    } else {
+        return v;
+    }
+}
 
 template <typename T, int D, int G, int NW, int U, bool PIPE>
 struct AttendCore {
@@ -150,10 +162,14 @@ struct AttendCore {
         }
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            float mn = m[j];
+            // the running maximum is kept uniform across the wave's row
+            // groups, so merging them at the end needs no rescaling
+            float mx = -INFINITY;
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (ok[u]) mn = fmaxf(mn, sc[u][j]);
+                if (ok[u]) mx = fmaxf(mx, sc[u][j]);
+            mx = rows_max<LPR>(mx);
+            const float mn = fmaxf(m[j], mx);
             const float corr = exp2_diff(m[j], mn);
             m[j] = mn;
             float lj = l[j] * corr;
@@ -208,24 +224,17 @@ struct AttendCore {
         }
     }
 
-    // Merges the row groups of each wave and stores the waves' states in LDS.
-    // The caller synchronises the block before combine().
+    // Merges the row groups of each wave (they share the running maximum, so
+    // their sums simply add) and stores the waves' states in LDS.  The caller
+    // synchronises the block before combine().
     template <int OFF>
     __device__ __forceinline__ void merge_groups() {
         if constexpr (OFF < kWave) {
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const float mo = xor_lanes<OFF>(m[j]);
-                const float lo = xor_lanes<OFF>(l[j]);
-                const float mn = fmaxf(m[j], mo);
-                const float c1 = exp2_diff(m[j], mn), c2 = exp2_diff(mo, mn);
-                l[j] = l[j] * c1 + lo * c2;
+                l[j] = pair_sum<OFF>(l[j]);
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    const float ao = xor_lanes<OFF>(acc[j][e]);
-                    acc[j][e] = acc[j][e] * c1 + ao * c2;
-                }
-                m[j] = mn;
+                for (int e = 0; e < EPL; ++e) acc[j][e] = pair_sum<OFF>(acc[j][e]);
             }
             merge_groups<OFF * 2>();
         }

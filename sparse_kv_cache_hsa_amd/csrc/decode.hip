@@ -161,7 +161,12 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             if (a.score_out) a.score_out[bh * max_pages + tid] = sc;
         }
         lds_barrier();  // the staged rows are dead; their LDS takes the sorted keys
-        if (K > 0) sort_topk<kBlock>(key, NP, K, comp_s, wave_tot, emit);
+        if (K > 0) {
+            if (K <= kWave)
+                topk_small<kBlock>(key, NP, K, comp_s, emit);
+            else
+                sort_topk<kBlock>(key, NP, K, comp_s, wave_tot, emit);
+        }
     } else {
         for (int p = tid; p < NP; p += kBlock) {
             float sc = page_bound<T, D, G>(sm_max, sm_min, max_pages, p, ch_s, k1, qsel);

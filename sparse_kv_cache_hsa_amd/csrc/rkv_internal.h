@@ -185,9 +185,26 @@ __device__ void block_topk_emit(Load load, int n, uint32_t thr, int take_eq, int
 // 2^-126).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The two values of lanes (lane & ~OFF, lane | OFF) of a 64-lane wave, for
+// OFF = 16 or 32, in every lane: `lo` from the lower lane, `hi` from the
+// upper one (the gfx950 lane-swap instructions, vector ALU only).
+template <int OFF>
+__device__ __forceinline__ void lane_pair(uint32_t v, uint32_t &lo, uint32_t &hi) {
+    static_assert(OFF == 16 || OFF == 32, "offset");
+    if constexpr (OFF == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap((int)v, (int)v, false, false);
+        lo = (uint32_t)r[0];
+        hi = (uint32_t)r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap((int)v, (int)v, false, false);
+        lo = (uint32_t)r[0];
+        hi = (uint32_t)r[1];
+    }
+}
+
 // Value of lane (lane ^ OFF) of a 64-lane wave: DPP quad permutes for 1 and
-// 2, the lane swizzle within 32-lane halves for 4 to 16, and a permute
-// across the halves for 32.
+// 2, the lane swizzle within 32-lane halves for 4 and 8, lane swaps for 16
+// and 32.
 template <int OFF>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
     static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "offset");
@@ -195,10 +212,37 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
         return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, true);
     } else if constexpr (OFF == 2) {
         return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, true);
-    } else if constexpr (OFF == 32) {
-        return (uint32_t)__shfl_xor((int)v, 32, kWave);
+    } else if constexpr (OFF >= 16) {
+        uint32_t lo, hi;
+        lane_pair<OFF>(v, lo, hi);
+        return (threadIdx.x & OFF) ? lo : hi;
     } else {
         return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (OFF << 10) | 0x1F);
+    }
+}
+
+// v(lane) + v(lane ^ OFF), the same bits in both lanes (lower lane's value
+// first).
+template <int OFF>
+__device__ __forceinline__ float pair_sum(float v) {
+    if constexpr (OFF >= 16) {
+        uint32_t lo, hi;
+        lane_pair<OFF>(__float_as_uint(v), lo, hi);
+        return __uint_as_float(lo) + __uint_as_float(hi);
+    } else {
+        const float o = __uint_as_float(lane_xor<OFF>(__float_as_uint(v)));
+        return (threadIdx.x & OFF) ? o + v : v + o;
+    }
+}
+
+template <int OFF>
+__device__ __forceinline__ float pair_max(float v) {
+    if constexpr (OFF >= 16) {
+        uint32_t lo, hi;
+        lane_pair<OFF>(__float_as_uint(v), lo, hi);
+        return fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+    } else {
+        return fmaxf(v, __uint_as_float(lane_xor<OFF>(__float_as_uint(v))));
     }
 }
 

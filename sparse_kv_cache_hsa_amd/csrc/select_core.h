@@ -33,6 +33,90 @@ __device__ __forceinline__ void load_group_q(const T *q, int64_t bh, float (*qs)
     for (int i = threadIdx.x; i < G * D; i += BLOCK) qs[i / D][i % D] = Elem<T>::ld(q, bh * G * D + i);
 }
 
+// ---- top-k by per-wave sorting ----------------------------------------------
+template <int J>
+__device__ __forceinline__ uint64_t key_xor(uint64_t v) {
+    const uint32_t lo = lane_xor<J>((uint32_t)v);
+    const uint32_t hi = lane_xor<J>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int J>
+__device__ __forceinline__ uint32_t key_xor(uint32_t v) {
+    return lane_xor<J>(v);
+}
+
+// One compare-exchange stage of a descending bitonic network at distance J:
+// the lane keeps the larger key when `up`, the smaller one otherwise.
+template <int J, typename K>
+__device__ __forceinline__ K bitonic_stage(K key, bool up) {
+    const K other = key_xor<J>(key);
+    return (up == (other > key)) ? other : key;
+}
+
+// Merge of size M (stages J = M/2 .. 1) of the full sort network.
+template <int M, int J, typename K>
+__device__ __forceinline__ K bitonic_merge(K key, int lane) {
+    key = bitonic_stage<J>(key, ((lane & M) == 0) == ((lane & J) == 0));
+    if constexpr (J > 1) key = bitonic_merge<M, J / 2>(key, lane);
+    return key;
+}
+
+// Half-cleaner cascade that sorts a bitonic wave sequence descending.
+template <int J, typename K>
+__device__ __forceinline__ K bitonic_clean(K key, int lane) {
+    key = bitonic_stage<J>(key, (lane & J) == 0);
+    if constexpr (J > 1) key = bitonic_clean<J / 2>(key, lane);
+    return key;
+}
+
+// Sorts the 64 keys of a wave in descending order (lane i gets the i-th
+// largest).  Distances 1 and 2 move through DPP, 4 to 16 through the lane
+// swizzle, 32 through a permute.
+template <typename K>
+__device__ __forceinline__ K wave_sort_desc(K key) {
+    const int lane = threadIdx.x & (kWave - 1);
+    key = bitonic_merge<2, 1>(key, lane);
+    key = bitonic_merge<4, 2>(key, lane);
+    key = bitonic_merge<8, 4>(key, lane);
+    key = bitonic_merge<16, 8>(key, lane);
+    key = bitonic_merge<32, 16>(key, lane);
+    key = bitonic_merge<64, 32>(key, lane);
+    return key;
+}
+
+// Top-K for K <= 64 of n <= BLOCK composite keys, key i held by thread i
+// (threads >= n pass 0, below every real key).  The waves holding keys sort
+// them into sorted_s (LDS, n rounded up to 64 uint64); after one barrier
+// wave 0 folds the sorted lists into the 64 largest keys (the element-wise
+// maximum of a descending list and a reversed one is bitonic and holds the
+// 64 largest of both), then sorts the K winners by index and calls
+// emit(pos, i) on its lanes pos < K, i ascending.  All threads must call it;
+// the caller synchronises the block before using what emit wrote.
+template <int BLOCK, typename Emit>
+__device__ void topk_small(uint64_t key, int n, int K, uint64_t *sorted_s, Emit emit) {
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
+    const int nw = (n + kWave - 1) / kWave;
+    if (w < nw) {
+        key = wave_sort_desc(key);
+        if (w > 0) sorted_s[tid] = key;
+    }
+    lds_barrier();
+    if (w == 0) {
+        uint64_t top = key;
+        for (int l = 1; l < nw; ++l) {
+            const uint64_t other = sorted_s[l * kWave + (kWave - 1 - lane)];
+            top = other > top ? other : top;
+            top = bitonic_clean<32>(top, lane);
+        }
+        // ~index of the K winners, descending = index ascending; the other
+        // lanes carry 0 and sort last
+        uint32_t inv = lane < K ? (uint32_t)top : 0u;
+        inv = wave_sort_desc(inv);
+        if (lane < K) emit(lane, (int)~inv);
+    }
+}
+
 // Rank count for n <= BLOCK composite keys comp_s[0..n) (LDS): every key is
 // compared with every other, the comparisons of one key spread over
 // BLOCK/n threads; then emit(pos, i) for the K largest, i ascending.
@@ -79,27 +163,35 @@ __device__ __forceinline__ void rank_channels(const float (*qs)[D], int k1, uint
                                               int *cnt_s, int *ch_s, float (*qsel)[D],
                                               int *wave_tot, float *qpm = nullptr) {
     const int tid = threadIdx.x;
+    uint64_t key = 0;
     if (tid < D) {
         float acc = 0.0f;
 #pragma unroll
         for (int j = 0; j < G; ++j) acc = acc + fabsf(qs[j][tid]);
         // acc >= +0, so its bits order like its value
-        comp_s[tid] = composite_key(__float_as_uint(acc), tid);
+        key = composite_key(__float_as_uint(acc), tid);
     }
-    lds_barrier();
-    rank_topk<BLOCK>(comp_s, D, k1, cnt_s, wave_tot, [&](int o, int c) { ch_s[o] = c; });
-    lds_barrier();
-    for (int t = tid; t < G * k1; t += BLOCK) {
-        const int j = t / k1, i = t % k1;
-        const float qv = qs[j][ch_s[i]];
-        qsel[j][i] = qv;
-        if (qpm) {
-            // by sign bit, so -0 goes to the Kmin side (both sides give a
-            // zero product there)
-            const bool neg = __float_as_uint(qv) >> 31;
-            qpm[i * 2 * G + j] = neg ? 0.0f : qv;
-            qpm[i * 2 * G + G + j] = neg ? qv : 0.0f;
+    auto emit = [&](int o, int c) {
+        ch_s[o] = c;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float qv = qs[j][c];
+            qsel[j][o] = qv;
+            if (qpm) {
+                // by sign bit, so -0 goes to the Kmin side (both sides give
+                // a zero product there)
+                const bool neg = __float_as_uint(qv) >> 31;
+                qpm[o * 2 * G + j] = neg ? 0.0f : qv;
+                qpm[o * 2 * G + G + j] = neg ? qv : 0.0f;
+            }
         }
+    };
+    if (k1 <= kWave) {
+        topk_small<BLOCK>(key, D, k1, comp_s, emit);
+    } else {
+        if (tid < D) comp_s[tid] = key;
+        lds_barrier();
+        rank_topk<BLOCK>(comp_s, D, k1, cnt_s, wave_tot, emit);
     }
     lds_barrier();
 }
@@ -302,46 +394,6 @@ __device__ __forceinline__ float staged_bound_exact(const uint16_t *stage, int n
 #pragma unroll
     for (int j = 0; j < G; ++j) tot = tot + s[j];
     return tot;
-}
-
-// ---- top-k by per-wave sorting ----------------------------------------------
-template <int J>
-__device__ __forceinline__ uint64_t key_xor(uint64_t v) {
-    const uint32_t lo = lane_xor<J>((uint32_t)v);
-    const uint32_t hi = lane_xor<J>((uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
-// One compare-exchange stage of the bitonic network (merge size K, distance
-// J): the lane keeps the larger key when its position in the K-block and its
-// J-bit agree, so the wave ends sorted in descending order.
-template <int K, int J>
-__device__ __forceinline__ uint64_t bitonic_stage(uint64_t key, int lane) {
-    const uint64_t other = key_xor<J>(key);
-    const bool keep_max = ((lane & K) == 0) == ((lane & J) == 0);
-    const bool take = keep_max ? (other > key) : (other < key);
-    return take ? other : key;
-}
-
-template <int K, int J>
-__device__ __forceinline__ uint64_t bitonic_merge(uint64_t key, int lane) {
-    key = bitonic_stage<K, J>(key, lane);
-    if constexpr (J > 1) key = bitonic_merge<K, J / 2>(key, lane);
-    return key;
-}
-
-// Sorts the 64 keys of a wave in descending order (lane i gets the i-th
-// largest).  Distances 1 and 2 move through DPP, 4 to 16 through the lane
-// swizzle, 32 through a permute.
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
-    const int lane = threadIdx.x & (kWave - 1);
-    key = bitonic_merge<2, 1>(key, lane);
-    key = bitonic_merge<4, 2>(key, lane);
-    key = bitonic_merge<8, 4>(key, lane);
-    key = bitonic_merge<16, 8>(key, lane);
-    key = bitonic_merge<32, 16>(key, lane);
-    key = bitonic_merge<64, 32>(key, lane);
-    return key;
 }
 
 // Top-K of n <= BLOCK composite keys, key i held by thread i (threads >= n
