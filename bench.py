@@ -57,6 +57,26 @@ def step_bytes(sess, rows_now, per_head_rows):
     return (q + summaries + out + append) * sess.n_layers + sum(kv), kv[0] + q + out
 
 
+def measured_copy_gbs(dev, nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Read + write bandwidth of a plain device-to-device copy: the practical
+    HBM ceiling on this device, reported beside the 8 TB/s spec."""
+    import torch
+    x = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = reps * 2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def counted_traffic(kernel: str, workload: str, build_id: str):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none for
@@ -210,8 +230,8 @@ def main():
     per_head_rows = [attended_rows(sess, sess.page_idx[l], rows_last) for l in range(sess.n_layers)]
     attended_seq_layer = sum(per_head_rows) / sess.Hkv       # per (sequence, layer)
     step_b, attend_b0 = step_bytes(sess, rows_last, per_head_rows)
-    log(f"[bench] algorithmic bytes per step {step_b / 1e9:.3f} GB, attended rows per "
-        f"(sequence, layer) {attended_seq_layer:.1f}")
+    log(f"[bench] algorithmic bytes per step {step_b / 1e9:.3f} GB, attended rows per step "
+        f"(all sequences and layers, per KV head) {attended_seq_layer:.1f}")
 
     # ---- dominant kernel ----------------------------------------------------
     # Fused path: a step is one decode_kernel launch per layer on this stream,
@@ -251,6 +271,9 @@ def main():
         f"{kern_gbs:.0f} GB/s; counted traffic "
         f"{'n/a' if traffic is None else f'{traffic / 1e6:.2f} MB/launch'}")
 
+    copy_gbs = measured_copy_gbs(dev)
+    log(f"[bench] measured device copy (1 GiB, read + write): {copy_gbs:.0f} GB/s")
+
     steps_per_s = 1e3 / ms_step
     result = {
         "metric": METRIC,
@@ -280,6 +303,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(kern_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "avg_launch_us": round(launch_us, 3),
+                     "measured_copy_gbs": round(copy_gbs, 1),
+                     "frac_of_measured_copy": round(kern_gbs / copy_gbs, 4),
                      "bytes_per_launch": int(bytes_launch)},
     }
     if not args.no_cpu_baseline:

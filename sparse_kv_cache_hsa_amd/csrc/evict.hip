@@ -15,9 +15,10 @@
 //                w window rows;
 //   6. compact : gather K/V rows into the paged cache; rebuild summaries.
 // The logits are computed with one thread per query row walking an LDS tile
-// of keys in channel order without multiply-add contraction, so they match a
-// sequential fp32 evaluation bit for bit; only expf may differ from another
-// library's in the last place.
+// of keys in channel order, so they match a sequential fp32 evaluation bit for
+// bit (fp32 inputs: separate multiply and add; bf16 inputs: fused
+// multiply-add, which is the same because the products are exact); only expf
+// may differ from another library's in the last place.
 //
 // Workspace (per call): logits Z[B][Hkv][L_max][R] fp32 (row-fastest so that
 // every pass reads it coalesced), per-tile row maxima, fp64 partial sums,
@@ -89,8 +90,15 @@ logits_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, const T *q_win
         float tmax = -INFINITY;
         for (int tt = 0; tt < nk; ++tt) {
             float dot = 0.0f;
+            if constexpr (sizeof(T) == 2) {
+                // bf16 q * bf16 k is exact in fp32, so the fused form rounds
+                // once per step exactly like dot + fl(q * k)
 #pragma unroll
-            for (int c = 0; c < D; ++c) dot = dot + qr[c] * ks[tt][c];
+                for (int c = 0; c < D; ++c) dot = __builtin_fmaf(qr[c], ks[tt][c], dot);
+            } else {
+#pragma unroll
+                for (int c = 0; c < D; ++c) dot = dot + qr[c] * ks[tt][c];
+            }
             const float z = dot * scale;
             Z[(bh * L_max + t0 + tt) * R + r] = z;
             if (t0 + tt <= last) tmax = fmaxf(tmax, z);
