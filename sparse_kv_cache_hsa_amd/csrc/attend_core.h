@@ -121,6 +121,35 @@ struct AttendCore {
         }
     }
 
+    // Same state as init(), from the queries already in LDS as fp32 (qs[j][c],
+    // exact widenings of the inputs).
+    __device__ __forceinline__ void init_lds(const float (*qs)[D], float qscale) {
+        lane = threadIdx.x & (kWave - 1);
+        w = threadIdx.x / kWave;
+        sub = lane % LPR;
+        rsub = lane / LPR;
+        qs_ = qscale;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float x[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) x[e] = qs[j][sub * EPL + e];
+            if constexpr (kPacked) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    qp[j][e] = (__float_as_uint(x[2 * e]) >> 16) |
+                               (__float_as_uint(x[2 * e + 1]) & 0xffff0000u);
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) qv[j][e] = x[e] * qscale;
+            }
+            m[j] = -INFINITY;
+            l[j] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[j][e] = 0.0f;
+        }
+    }
+
     __device__ __forceinline__ void issue(const uint32_t *row_s, int nrows, const T *k_pool,
                                           const T *v_pool, int base, uint4 *kr, uint4 *vr,
                                           bool *ok) const {

@@ -62,6 +62,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     __shared__ int32_t sel_s[RKV_MAX_K2];
     __shared__ int32_t blk_s[kFusedMaxPages];
     __shared__ int cnt_s[kBlock];
+    __shared__ uint64_t sort_s[kBlock];  // page keys of the staged path's top-k
     __shared__ uint32_t hist[256];
     __shared__ int wave_tot[kNW];
     __shared__ int sh[2];
@@ -160,12 +161,15 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             key = composite_key(ordered_key(sc), tid);
             if (a.score_out) a.score_out[bh * max_pages + tid] = sc;
         }
-        lds_barrier();  // the staged rows are dead; their LDS takes the sorted keys
+        // the sorted keys have LDS of their own, so no barrier is needed
+        // between scoring and sorting
         if (K > 0) {
             if (K <= kWave)
-                topk_small<kBlock>(key, NP, K, comp_s, emit);
+                topk_small<kBlock>(key, NP, K, sort_s, emit);
             else
-                sort_topk<kBlock>(key, NP, K, comp_s, wave_tot, emit);
+                sort_topk<kBlock>(key, NP, K, sort_s, wave_tot, emit);
+        } else {
+            lds_barrier();
         }
     } else {
         for (int p = tid; p < NP; p += kBlock) {
@@ -196,7 +200,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         row_s[f] = r;
     }
     Core core;
-    core.init(q, bh, a.qscale);
+    core.init_lds(qs, a.qscale);
     __syncthreads();
     core.stream(row_s, nrows, k_pool, v_pool);
     lds_barrier();  // the row table is dead; its LDS now takes the states
