@@ -296,3 +296,61 @@ def test_prefill_evict_matches_oracle(dtype, pool):
                 np.testing.assert_array_equal(gmax, smax)
                 np.testing.assert_array_equal(gmin, smin)
     print(f"near-tie boundary swaps: {swaps}")
+
+
+# The pages' ablation axes as parameterisations of the same kernels: Quest-only
+# (k1 = d: every channel, so the page bound is the full box bound), SparQ-only
+# (page size 1: the bound is the partial dot product of the k1 channels) and
+# Exact-TopK (both: the exact GQA-summed score of every token).
+PARAM_CASES = {
+    "quest": (BF16, 2, 8, 4, 128, 16, 128, 32, [3000, 2000], 200),
+    "sparq": (BF16, 2, 8, 4, 128, 1, 32, 256, [1500, 700], 1600),
+    "exact": (BF16, 2, 8, 4, 128, 1, 128, 512, [1800, 900], 1900),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PARAM_CASES))
+@pytest.mark.parametrize("mode", ["decode", "step"])
+def test_selection_parameterisations(name, mode, path):
+    case = PARAM_CASES[name]
+    if path == "fused" and not fused_supported(case):
+        pytest.skip("shape outside the fused kernel's limits")
+    run_decode_case(case, 3000 + len(name), mode=mode)
+
+
+def test_exact_topk_is_the_top_of_the_true_scores():
+    """With P = 1 and k1 = d the selected tokens are the k2 largest exact
+    scores sum_j q_j . k_t (checked in float64 away from near ties)."""
+    rkv = lib()
+    dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages = PARAM_CASES["exact"]
+    Lmax = max(lens)
+    K = rand((B, Hkv, Lmax, d), 91, dtype, 1.5)
+    q = rand((B, Hkv * G, d), 92, dtype)
+    g = rkv.gqa(Hkv, G, d)
+    cache, summ = make_cache(Hkv, d, P, max_pages, [max_pages] * B, dtype, 9)
+    fill_cache(g, cache, summ, K.cuda(), K.cuda(), lens)
+    pidx = torch.zeros((B, Hkv, k2), dtype=torch.int32, device="cuda")
+    ws = rkv.hsa_workspace(g, B, P, max_pages, k1, k2, "cuda")
+    rkv.rkv_hsa_select(g, q.cuda(), torch.tensor(lens, dtype=torch.int32, device="cuda"), P, summ,
+                       k1, k2, pidx, ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(Hkv):
+            s = (q[b, h * G:(h + 1) * G].double() @ K[b, h, :lens[b]].double().T).sum(0).numpy()
+            order = np.argsort(-s, kind="stable")
+            kth, nxt = s[order[k2 - 1]], s[order[k2]]
+            if abs(kth - nxt) <= 1e-5 * abs(kth):
+                continue  # float64 and the fp32 order may rank a near tie differently
+            np.testing.assert_array_equal(pidx[b, h].cpu().numpy(), np.sort(order[:k2]))
+
+
+def test_selection_overlap_measurement_runs():
+    """The overlap measurement on the tiny workload: exact top-k agrees with
+    itself and every method's recall and attention mass are fractions."""
+    from sparse_kv_cache_hsa_amd import overlap
+    res = overlap.measure(workloads.TINY, steps=2)
+    assert res["exact"]["recall_vs_exact_min"] == 1.0
+    for m in ("hsa", "quest", "sparq", "exact"):
+        for key in ("recall_vs_exact_mean", "attention_mass_mean"):
+            assert 0.0 <= res[m][key] <= 1.0 + 1e-6
+    assert res["exact"]["attention_mass_mean"] >= res["hsa"]["attention_mass_mean"] - 1e-6
