@@ -107,6 +107,120 @@ logits_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, const T *q_win
     }
 }
 
+// Register-tiled logits for 16-byte aligned inputs.  A block covers 128
+// window rows (row group blockIdx.x / ntiles) against 64 keys (tile
+// blockIdx.x % ntiles); each of its 256 threads computes 4 rows x 8 keys.
+// Channels are staged through LDS 32 at a time (channel-major, fp32), and
+// every dot product still runs over the channels in ascending order, one
+// rounding per step, exactly as in logits_kernel -- only the number of LDS
+// reads per multiply-add drops (3 vector reads per 32 of them instead of 8).
+constexpr int kLtRows = 128, kLtKeys = 64, kLtChunk = 32;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+logits_tiled_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, const T *q_win,
+                    const T *k, float scale, int ntiles, float *Z, float *TM) {
+    constexpr int V = Vec16<T>::N;            // elements per 16-byte load
+    constexpr int VPR = kLtChunk / V;         // 16-byte loads per row and chunk
+    __shared__ __align__(16) float qs[kLtChunk][kLtRows];
+    __shared__ __align__(16) float ks[kLtChunk][kLtKeys];
+    __shared__ float tm_s[kLtKeys / 8][kLtRows];
+    const int b = blockIdx.z, h = blockIdx.y, tid = threadIdx.x;
+    const int tile = blockIdx.x % ntiles, r0 = (blockIdx.x / ntiles) * kLtRows;
+    const int64_t L = seq.L[b];
+    if (seq.keep[b] >= L) return;
+    const int64_t t0 = (int64_t)tile * kLtKeys;
+    if (t0 >= L) return;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int nk = (int)min<int64_t>(kLtKeys, L - t0);
+    const int rt = tid & 31, kt = tid >> 5;   // rows rt*4.., keys kt*8..
+    const T *qb = q_win + (bh * R) * D;
+    const T *kb = k + (bh * L_max + t0) * D;
+    float acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+    for (int c0 = 0; c0 < D; c0 += kLtChunk) {
+        for (int i = tid; i < kLtRows * VPR; i += 256) {
+            const int r = i / VPR, v = i % VPR;
+            float x[V];
+            if (r0 + r < R) {
+                Vec16<T>::unpack(*(const uint4 *)(qb + (int64_t)(r0 + r) * D + c0 + v * V), x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) x[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) qs[v * V + e][r] = x[e];
+        }
+        for (int i = tid; i < kLtKeys * VPR; i += 256) {
+            const int t = i / VPR, v = i % VPR;
+            float x[V];
+            if (t < nk) {
+                Vec16<T>::unpack(*(const uint4 *)(kb + (int64_t)t * D + c0 + v * V), x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) x[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) ks[v * V + e][t] = x[e];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int c = 0; c < kLtChunk; ++c) {
+            const float4 qv = *(const float4 *)&qs[c][rt * 4];
+            const float4 ka = *(const float4 *)&ks[c][kt * 8];
+            const float4 kc = *(const float4 *)&ks[c][kt * 8 + 4];
+            const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
+            const float kk[8] = {ka.x, ka.y, ka.z, ka.w, kc.x, kc.y, kc.z, kc.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if constexpr (sizeof(T) == 2)
+                        acc[i][j] = __builtin_fmaf(qq[i], kk[j], acc[i][j]);
+                    else
+                        acc[i][j] = acc[i][j] + qq[i] * kk[j];
+                }
+        }
+        __syncthreads();
+    }
+    float tmax[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmax[i] = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int tt = kt * 8 + j;
+        if (tt >= nk) break;
+        float z[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            z[i] = acc[i][j] * scale;
+            const int r = r0 + rt * 4 + i;
+            const int64_t last = L - w + (r % w);
+            if (r < R && t0 + tt <= last) tmax[i] = fmaxf(tmax[i], z[i]);
+        }
+        float *zr = Z + (bh * L_max + t0 + tt) * R + r0 + rt * 4;
+        if (r0 + rt * 4 + 3 < R && ((R & 3) == 0)) {
+            *(float4 *)zr = make_float4(z[0], z[1], z[2], z[3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (r0 + rt * 4 + i < R) zr[i] = z[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tm_s[kt][rt * 4 + i] = tmax[i];
+    __syncthreads();
+    if (tid < kLtRows && r0 + tid < R) {
+        float m = tm_s[0][tid];
+#pragma unroll
+        for (int q = 1; q < kLtKeys / 8; ++q) m = fmaxf(m, tm_s[q][tid]);
+        TM[(bh * ntiles + tile) * R + r0 + tid] = m;
+    }
+}
+
 __global__ void __launch_bounds__(256)
 rowmax_kernel(int Hkv, int R, EvictSeq seq, int ntiles, const float *TM, float *M) {
     const int b = blockIdx.y, h = blockIdx.x;
@@ -285,8 +399,14 @@ int launch_t(const rkv_gqa &g, int B, const EvictSeq &seq, int64_t L_max, int w,
     }
     const int blocks_t = (int)((L_max + 255) / 256);
 
-    logits_kernel<T, D><<<dim3(l.ntiles, Hkv, B), kLogitsBlock, 0, s>>>(
-        Hkv, R, w, L_max, seq, (const T *)q_win, (const T *)k, scale, l.ntiles, Z, TM);
+    if (((uintptr_t)q_win & 15u) == 0 && ((uintptr_t)Z & 15u) == 0) {
+        const int rgroups = (R + kLtRows - 1) / kLtRows;
+        logits_tiled_kernel<T, D><<<dim3(l.ntiles * rgroups, Hkv, B), 256, 0, s>>>(
+            Hkv, R, w, L_max, seq, (const T *)q_win, (const T *)k, scale, l.ntiles, Z, TM);
+    } else {
+        logits_kernel<T, D><<<dim3(l.ntiles, Hkv, B), kLogitsBlock, 0, s>>>(
+            Hkv, R, w, L_max, seq, (const T *)q_win, (const T *)k, scale, l.ntiles, Z, TM);
+    }
     rowmax_kernel<<<dim3(Hkv, B), 256, 0, s>>>(Hkv, R, seq, l.ntiles, TM, M);
     rowsum_kernel<<<dim3(l.nch, Hkv, B), 256, 0, s>>>(Hkv, R, w, L_max, seq, l.nch, Z, M, PL);
     rowsum_final_kernel<<<dim3(Hkv, B), 256, 0, s>>>(Hkv, R, seq, l.nch, PL, ell);
