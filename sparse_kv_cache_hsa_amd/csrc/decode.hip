@@ -58,7 +58,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     __shared__ __align__(16) float qpm_s[D * 2 * G];
     constexpr bool kPacked = std::is_same<T, uint16_t>::value;
     __shared__ int ch_s[D];
-    __shared__ T ovr_hi[D], ovr_lo[D];
+    __shared__ T ovr_hi[D], ovr_lo[D], xs[D];
     __shared__ int32_t sel_s[RKV_MAX_K2];
     __shared__ int32_t blk_s[kFusedMaxPages];
     __shared__ int cnt_s[kBlock];
@@ -84,46 +84,19 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     T *sm_max = summ + bh * 2 * D * max_pages;
     T *sm_min = sm_max + (int64_t)D * max_pages;
 
-    // 1. append row n-1 and fold it into its page summary (first of equal
-    //    values kept: strict comparisons, as in a rebuild); keep the page's new
-    //    summary in LDS for this block's own scoring.  Every load of this
-    //    phase (the new row, the old summary, the page table row, the
-    //    queries) is issued before the first store, so the phase costs one
-    //    memory round trip.
+    // 1. the loads that do not depend on the row count: the new K/V row and
+    //    the queries (they share a memory round trip with the row count).
     const bool append = k_new != nullptr && n > 0;
     const int p_new = append ? (int)((n - 1) / P) : -1;
     const int slot = append ? (int)(n - 1 - (int64_t)p_new * P) : 0;
     const int64_t im = (int64_t)tid * max_pages + p_new;
-    T x{}, vx{}, omax{}, omin{};
-    int32_t blk_new = -1;
-    if (append && tid < D) {
-        blk_new = a.page_table[(int64_t)b * max_pages + p_new];
+    T x{}, vx{};
+    if (k_new != nullptr && tid < D) {
         x = k_new[bh * D + tid];
         vx = v_new[bh * D + tid];
-        if (slot != 0) {
-            omax = sm_max[im];
-            omin = sm_min[im];
-        }
+        xs[tid] = x;
     }
-    for (int p = tid; p < NP; p += kBlock) blk_s[p] = a.page_table[(int64_t)b * max_pages + p];
     load_group_q<T, D, G, kBlock>(q, bh, qs);
-    if (append && tid < D) {
-        T nmax = x, nmin = x;
-        if (slot != 0) {
-            const float fx = Elem<T>::ld(&x, 0);
-            nmax = fx > Elem<T>::ld(&omax, 0) ? x : omax;
-            nmin = fx < Elem<T>::ld(&omin, 0) ? x : omin;
-        }
-        ovr_hi[tid] = nmax;
-        ovr_lo[tid] = nmin;
-        if (blk_new >= 0 && blk_new < a.num_blocks) {
-            const int64_t dst = (((int64_t)blk_new * a.Hkv + h) * P + slot) * D + tid;
-            k_pool[dst] = x;
-            v_pool[dst] = vx;
-            sm_max[im] = nmax;
-            sm_min[im] = nmin;
-        }
-    }
     lds_barrier();
 
     // 2. channels
@@ -131,10 +104,12 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
                                 kPacked ? qpm_s : nullptr);
     if (a.chan_out && tid < k1) a.chan_out[bh * k1 + tid] = ch_s[tid];
 
-    // 3-4. page bounds and page top-k2.  The summaries of the chosen channels
-    //      are staged in LDS by the whole block when they fit; the page holding
-    //      the appended row takes this block's new summary from LDS (its
-    //      global stores need not have landed).
+    // 3. the second memory round trip: the page-table row, the appended
+    //    page's old summary and, when they fit, the summaries of the chosen
+    //    channels; then the appended row is folded in (first of equal values
+    //    kept: strict comparisons, as in a rebuild) and stored.  The page
+    //    holding the appended row is scored from LDS with its new summary.
+    // 4. page bounds and page top-k2.
     const int K = min(k2, NP);
     constexpr int V = 16 / (int)sizeof(T);
     const bool staged = (size_t)2 * k1 * ((NP + V - 1) / V * V) * sizeof(T) <= kStageBytes &&
@@ -143,12 +118,53 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         sel_s[o] = i;
         if (a.page_out) a.page_out[bh * k2 + o] = i;
     };
+    auto fold = [&](T xv, T omax, T omin, T &nmax, T &nmin) {
+        nmax = xv;
+        nmin = xv;
+        if (slot != 0) {
+            const float fx = Elem<T>::ld(&xv, 0);
+            nmax = fx > Elem<T>::ld(&omax, 0) ? xv : omax;
+            nmin = fx < Elem<T>::ld(&omin, 0) ? xv : omin;
+        }
+    };
+    auto store_append = [&](T nmax, T nmin) {
+        const int32_t blk = blk_s[p_new];
+        if (blk >= 0 && blk < a.num_blocks) {
+            const int64_t dst = (((int64_t)blk * a.Hkv + h) * P + slot) * D + tid;
+            k_pool[dst] = x;
+            v_pool[dst] = vx;
+            sm_max[im] = nmax;
+            sm_min[im] = nmin;
+        }
+    };
+    T omax{}, omin{};
     if (staged) {
+        dma_copy_i32<kBlock>(a.page_table + (int64_t)b * max_pages, NP, blk_s);
+        T cx{}, comax{}, comin{};
+        if (append && tid < D && slot != 0) {
+            omax = sm_max[im];
+            omin = sm_min[im];
+        }
+        if (append && tid < k1) {
+            const int c = ch_s[tid];
+            cx = xs[c];
+            if (slot != 0) {
+                comax = sm_max[(int64_t)c * max_pages + p_new];
+                comin = sm_min[(int64_t)c * max_pages + p_new];
+            }
+        }
         const int npad = stage_summaries<T, kBlock>(sm_max, sm_min, max_pages, 0, NP, ch_s, k1, stage);
         lds_barrier();
-        if (p_new >= 0 && tid < k1) {
-            stage[(int64_t)tid * npad + p_new] = ovr_hi[ch_s[tid]];
-            stage[(int64_t)(k1 + tid) * npad + p_new] = ovr_lo[ch_s[tid]];
+        if (append && tid < k1) {
+            T nmax, nmin;
+            fold(cx, comax, comin, nmax, nmin);
+            stage[(int64_t)tid * npad + p_new] = nmax;
+            stage[(int64_t)(k1 + tid) * npad + p_new] = nmin;
+        }
+        if (append && tid < D) {
+            T nmax, nmin;
+            fold(x, omax, omin, nmax, nmin);
+            store_append(nmax, nmin);
         }
         lds_barrier();
         uint64_t key = 0;
@@ -172,6 +188,20 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             lds_barrier();
         }
     } else {
+        for (int p = tid; p < NP; p += kBlock) blk_s[p] = a.page_table[(int64_t)b * max_pages + p];
+        if (append && tid < D && slot != 0) {
+            omax = sm_max[im];
+            omin = sm_min[im];
+        }
+        lds_barrier();
+        if (append && tid < D) {
+            T nmax, nmin;
+            fold(x, omax, omin, nmax, nmin);
+            ovr_hi[tid] = nmax;
+            ovr_lo[tid] = nmin;
+            store_append(nmax, nmin);
+        }
+        lds_barrier();
         for (int p = tid; p < NP; p += kBlock) {
             float sc = page_bound<T, D, G>(sm_max, sm_min, max_pages, p, ch_s, k1, qsel);
             if (p == p_new) sc = page_bound_ovr<T, D, G>(ch_s, k1, qsel, ovr_hi, ovr_lo);

@@ -310,6 +310,17 @@ __device__ __forceinline__ void stage_rows(const T *smax, const T *smin, int max
     }
 }
 
+// dst[i] = src[i] for i < n (int32, dst in LDS) with direct global-to-LDS
+// loads; the caller waits for them (vmcnt) and synchronises the block.
+template <int BLOCK>
+__device__ __forceinline__ void dma_copy_i32(const int32_t *src, int n, int32_t *dst) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int base = threadIdx.x - lane; base < n; base += BLOCK)
+        if (base + lane < n)
+            __builtin_amdgcn_global_load_lds(src + base + lane, (lds_void *)(dst + base), 4, 0, 0);
+}
+
 template <typename T, int BLOCK>
 __device__ __forceinline__ int stage_summaries(const T *smax, const T *smin, int max_pages, int p0,
                                                int n, const int *ch_s, int k1, T *stage) {
