@@ -51,8 +51,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     using Core = AttendCore<T, D, G, kNW, 4, false>;
     constexpr size_t kKeyBytes = sizeof(uint64_t) * kFusedMaxPages;
     constexpr size_t kRowBytes = sizeof(uint32_t) * kFusedMaxRows;
-    constexpr size_t kCoreBytes = sizeof(typename Core::Shared);
-    constexpr size_t kUnion = cmax(cmax(kStageBytes, kKeyBytes), cmax(kRowBytes, kCoreBytes));
+    constexpr size_t kUnion = cmax(cmax(kStageBytes, kKeyBytes), kRowBytes);
     __shared__ float qs[G][D];
     __shared__ float qsel[G][D];
     __shared__ __align__(16) float qpm_s[D * 2 * G];
@@ -67,13 +66,15 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     __shared__ int wave_tot[kNW];
     __shared__ int sh[2];
     // staged summaries or page keys (selection), then the row table
-    // (attention), then the waves' partial states (final merge): never live
-    // at the same time
+    // (attention): never live at the same time
     __shared__ __align__(16) unsigned char u_s[kUnion];
     T *stage = (T *)u_s;
     uint64_t *comp_s = (uint64_t *)u_s;
     uint32_t *row_s = (uint32_t *)u_s;
-    typename Core::Shared &csh = *(typename Core::Shared *)u_s;
+    // the waves' partial attention states have LDS of their own, so a wave
+    // stores its state as soon as its own rows are done while other waves
+    // still read the row table
+    __shared__ typename Core::Shared csh;
 
     const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
     const int P = a.P, k1 = a.k1, k2 = a.k2, max_pages = a.max_pages;
@@ -233,7 +234,6 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     core.init_lds(qs, a.qscale);
     __syncthreads();
     core.stream(row_s, nrows, k_pool, v_pool);
-    lds_barrier();  // the row table is dead; its LDS now takes the states
     core.to_shared(csh);
     lds_barrier();
     Core::combine(csh, [&](int j, int c, float M, float Ls, float A) {
