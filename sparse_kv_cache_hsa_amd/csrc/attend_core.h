@@ -14,14 +14,17 @@
 //     wave reads RPW = 64/LPR rows per load and U loads of K and of V per
 //     iteration; waves take iterations round-robin;
 //   - each lane holds its EPL channels of the G query heads (the G heads share
-//     every K/V load) and an online-softmax state per head in the log2 domain;
+//     every K/V load) and an online-softmax state per head in the log2 domain
+//     (hardware exp2); the running maximum is kept uniform across the row
+//     groups of a wave, so their sums merge without rescaling;
 //   - bf16 dot products use the packed bf16 dot instruction (exact products,
 //     fp32 accumulation) with the query kept as exact bf16 pairs and the
 //     scale*log2(e) factor applied to the finished dot product; fp32 inputs
 //     use fp32 multiply-adds with a pre-scaled query;
 //   - dot products are finished inside the LPR lanes of a row with DPP
-//     butterflies; at the end the row groups of a wave are merged with
-//     shuffles and the waves through LDS, in a fixed order.
+//     butterflies; at the end the row groups of a wave are summed with lane
+//     swaps and the waves are merged through LDS in a fixed order, so the
+//     result does not depend on timing.
 #pragma once
 
 #include <type_traits>
