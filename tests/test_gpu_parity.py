@@ -34,6 +34,11 @@ DECODE_CASES = [
     (F32, 1, 2, 2, 128, 32, 128, 1024, [8000], 260),
     (BF16, 1, 1, 4, 128, 4, 32, 50, [20000], 5000),
     (F32, 4, 2, 8, 64, 3, 5, 7, [1, 2, 3, 250], 100),
+    # the largest page size, one channel and one page, a cache filled to
+    # exactly its capacity (max_pages * P rows)
+    (BF16, 2, 2, 4, 128, 256, 1, 1, [3000, 256], 16),
+    (BF16, 3, 2, 2, 64, 16, 1, 1, [1, 16, 17], 4),
+    (BF16, 2, 2, 4, 128, 16, 32, 64, [2048, 2047], 128),
 ]
 
 
