@@ -115,10 +115,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     constexpr int V = 16 / (int)sizeof(T);
     const bool staged = (size_t)2 * k1 * ((NP + V - 1) / V * V) * sizeof(T) <= kStageBytes &&
                         NP <= kBlock;
-    auto emit = [&](int o, int i) {
-        sel_s[o] = i;
-        if (a.page_out) a.page_out[bh * k2 + o] = i;
-    };
+    auto emit = [&](int o, int i) { sel_s[o] = i; };
     auto fold = [&](T xv, T omax, T omin, T &nmax, T &nmin) {
         nmax = xv;
         nmin = xv;
@@ -212,8 +209,6 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         lds_barrier();
         topk_ascending<kBlock>(comp_s, NP, K, cnt_s, hist, sh, wave_tot, emit);
     }
-    if (a.page_out)
-        for (int o = K + tid; o < k2; o += kBlock) a.page_out[bh * k2 + o] = -1;
     lds_barrier();
 
     // 5. resolve the rows of the selected pages, then stream them.  The full
@@ -239,6 +234,10 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     Core::combine(csh, [&](int j, int c, float M, float Ls, float A) {
         a.out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
     });
+    // the page list goes out last: stored earlier, it would hold up the full
+    // barrier before the stream (which waits for this wave's stores)
+    if (a.page_out)
+        for (int o = tid; o < k2; o += kBlock) a.page_out[bh * k2 + o] = o < K ? sel_s[o] : -1;
 }
 
 template <typename T, int D, int G>
