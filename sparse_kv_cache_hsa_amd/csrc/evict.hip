@@ -238,13 +238,47 @@ rowmax_kernel(int Hkv, int R, EvictSeq seq, int ntiles, const float *TM, float *
 __global__ void __launch_bounds__(256)
 rowsum_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, int nch, const float *Z,
               const float *M, double *PL) {
-    const int b = blockIdx.z, h = blockIdx.y, ch = blockIdx.x;
+    __shared__ double part_s[256];
+    const int b = blockIdx.z, h = blockIdx.y, ch = blockIdx.x, tid = threadIdx.x;
     const int64_t L = seq.L[b];
     if (seq.keep[b] >= L) return;
     const int64_t bh = (int64_t)b * Hkv + h;
     const int64_t t0 = (int64_t)ch * kCH;
     const int64_t t1 = min<int64_t>(L, t0 + kCH);
-    for (int r = threadIdx.x; r < R; r += 256) {
+    if (R <= 128) {
+        // several threads per row, each over a contiguous part of the chunk;
+        // the parts are added in part order
+        const int parts = 256 / R;
+        const int r = tid % R, part = tid / R;
+        double acc = 0.0;
+        if (part < parts) {
+            const int64_t last = L - w + (r % w);
+            const int64_t te = min<int64_t>(t1, last + 1);
+            const int64_t span = (kCH + parts - 1) / parts;
+            const int64_t a0 = t0 + part * span, a1 = min<int64_t>(te, a0 + span);
+            const float mr = M[bh * R + r];
+            // batches of loads in flight; the sum stays in key order
+            constexpr int kBatch = 8;
+            for (int64_t tb = a0; tb < a1; tb += kBatch) {
+                float z[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u)
+                    z[u] = tb + u < a1 ? Z[(bh * L_max + tb + u) * R + r] : 0.0f;
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u)
+                    if (tb + u < a1) acc += (double)expf(z[u] - mr);
+            }
+        }
+        part_s[tid] = acc;
+        __syncthreads();
+        if (tid < R) {
+            double sum = 0.0;
+            for (int q = 0; q < parts; ++q) sum += part_s[q * R + tid];
+            PL[(bh * nch + ch) * R + tid] = sum;
+        }
+        return;
+    }
+    for (int r = tid; r < R; r += 256) {
         const int64_t last = L - w + (r % w);
         const int64_t te = min<int64_t>(t1, last + 1);
         const float mr = M[bh * R + r];
@@ -296,6 +330,63 @@ colsum_kernel(int Hkv, int G, int w, int64_t L_max, EvictSeq seq, const float *Z
         a = a + aj;
     }
     A[bh * L_max + t] = a;
+}
+
+// Column sums for R <= 128 (at most 34 KB of LDS): a block takes 64 prefix keys; its threads compute
+// p = expf(z - m) / ell for whole Z rows (coalesced over r) into LDS, then one
+// thread per key adds them over i, then j, in the definition's order.
+constexpr int kCsKeys = 64;
+
+__global__ void __launch_bounds__(256)
+colsum_tiled_kernel(int Hkv, int G, int w, int64_t L_max, EvictSeq seq, const float *Z,
+                    const float *M, const float *ell, float *A) {
+    extern __shared__ float sm[];
+    const int R = G * w, RS = R + 1;  // padded row stride: conflict-free column reads
+    float *Ms = sm, *Es = sm + R, *ps = sm + 2 * R;
+    const int b = blockIdx.z, h = blockIdx.y, tid = threadIdx.x;
+    const int64_t L = seq.L[b];
+    if (seq.keep[b] >= L) return;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int64_t t0 = (int64_t)blockIdx.x * kCsKeys;
+    const int64_t npre = L - w;
+    if (t0 >= npre) return;
+    const int nk = (int)min<int64_t>(kCsKeys, npre - t0);
+    for (int r = tid; r < R; r += 256) {
+        Ms[r] = M[bh * R + r];
+        Es[r] = ell[bh * R + r];
+    }
+    __syncthreads();
+    const int per = 256 / R;  // keys per pass
+    if (tid < per * R) {
+        // the loads of a batch are issued together, then used
+        constexpr int kBatch = 8;
+        const int r = tid % R;
+        const float mr = Ms[r], er = Es[r];
+        for (int tb = tid / R; tb < nk; tb += per * kBatch) {
+            float z[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int tt = tb + u * per;
+                z[u] = tt < nk ? Z[(bh * L_max + t0 + tt) * R + r] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int tt = tb + u * per;
+                if (tt < nk) ps[tt * RS + r] = expf(z[u] - mr) / er;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < nk) {
+        const float *pr = ps + tid * RS;
+        float a = 0.0f;
+        for (int j = 0; j < G; ++j) {
+            float aj = 0.0f;
+            for (int i = 0; i < w; ++i) aj = aj + pr[j * w + i];
+            a = a + aj;
+        }
+        A[bh * L_max + t0 + tid] = a;
+    }
 }
 
 __global__ void __launch_bounds__(256)
@@ -410,8 +501,15 @@ int launch_t(const rkv_gqa &g, int B, const EvictSeq &seq, int64_t L_max, int w,
     rowmax_kernel<<<dim3(Hkv, B), 256, 0, s>>>(Hkv, R, seq, l.ntiles, TM, M);
     rowsum_kernel<<<dim3(l.nch, Hkv, B), 256, 0, s>>>(Hkv, R, w, L_max, seq, l.nch, Z, M, PL);
     rowsum_final_kernel<<<dim3(Hkv, B), 256, 0, s>>>(Hkv, R, seq, l.nch, PL, ell);
-    colsum_kernel<<<dim3(blocks_t, Hkv, B), 256, 2 * R * sizeof(float), s>>>(
-        Hkv, G, w, L_max, seq, Z, M, ell, A);
+    if (R <= 128) {
+        const int tiles = (int)((L_max + kCsKeys - 1) / kCsKeys);
+        const size_t lds = (2 * R + (size_t)kCsKeys * (R + 1)) * sizeof(float);
+        colsum_tiled_kernel<<<dim3(tiles, Hkv, B), 256, lds, s>>>(Hkv, G, w, L_max, seq, Z, M,
+                                                                 ell, A);
+    } else {
+        colsum_kernel<<<dim3(blocks_t, Hkv, B), 256, 2 * R * sizeof(float), s>>>(
+            Hkv, G, w, L_max, seq, Z, M, ell, A);
+    }
     maxpool_kernel<<<dim3(blocks_t, Hkv, B), 256, 0, s>>>(Hkv, w, L_max, seq, pool_kernel / 2, A, pl);
     keep_kernel<<<dim3(Hkv, B), kKeepBlock, 0, s>>>(Hkv, w, L_max, seq, pl, kept, kstride, nold,
                                                     nnew, seq_lens_out);
