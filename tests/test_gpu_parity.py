@@ -358,3 +358,36 @@ def test_selection_overlap_measurement_runs():
     for m in ("hsa", "quest", "sparq", "exact"):
         for key in ("recall_vs_exact_mean", "attention_mass_mean"):
             assert 0.0 <= res[m][key] <= 1.0 + 1e-6
+
+
+def _random_cases(n, seed):
+    """Seeded shape combinations inside the documented limits."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        dtype = BF16 if rng.random() < 0.7 else F32
+        d = int(rng.choice([64, 128]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2, 3, 8]))
+        B = int(rng.integers(1, 5))
+        P = int(rng.choice([1, 2, 3, 8, 16, 32, 64]))
+        k1 = int(rng.integers(1, d + 1))
+        lens = [int(x) for x in rng.integers(0, 2500, B)]
+        need = max(n_pages(n, P) for n in lens) + 1
+        max_pages = int(min(2048, need + rng.integers(0, 8)))
+        lens = [min(n, max_pages * P) for n in lens]
+        k2 = int(rng.integers(1, min(300, max(2, need)) + 1))
+        cases.append((dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages))
+    return cases
+
+
+RANDOM_CASES = _random_cases(16, 2024)
+
+
+@pytest.mark.parametrize("ci", range(len(RANDOM_CASES)))
+@pytest.mark.parametrize("mode", ["decode", "step"])
+def test_random_shapes_match_oracle(ci, mode, path):
+    case = RANDOM_CASES[ci]
+    if path == "fused" and not fused_supported(case):
+        pytest.skip("shape outside the fused kernel's limits")
+    run_decode_case(case, 5000 + ci, mode=mode)
