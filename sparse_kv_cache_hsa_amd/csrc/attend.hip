@@ -80,27 +80,55 @@ attend_kernel(AttArgs a, const T *k_pool, const T *v_pool, const T *q) {
     }
 }
 
-// Combines the splits of every (sequence, KV head) in split order.
+// Combines the splits of one (sequence, KV head, query head of the group) in
+// split order: block (h, b, j), one thread per channel.  The split weights
+// 2^(m_s - M) are computed once into LDS; each channel then sums its split
+// partials with batches of loads in flight.
+constexpr int kMergeMaxSplits = 1024;
+
 template <int D, int G>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(D)
 attend_merge_kernel(int Hkv, int n_splits, const float *part, float *out) {
-    const int b = blockIdx.y, h = blockIdx.x;
+    __shared__ float cw_s[kMergeMaxSplits];
+    __shared__ float red_s[D];
+    __shared__ float ML_s[2];
+    const int h = blockIdx.x, b = blockIdx.y, j = blockIdx.z, c = threadIdx.x;
     const int64_t bh = (int64_t)b * Hkv + h;
-    for (int t = threadIdx.x; t < G * D; t += 256) {
-        const int j = t / D, c = t % D;
-        const float *base_p = part + (bh * n_splits * G + j) * (D + 2);
-        const int64_t stride = (int64_t)G * (D + 2);
+    const int64_t stride = (int64_t)G * (D + 2);
+    const float *base_p = part + (bh * n_splits * G + j) * (D + 2);
+    // M = max over the splits' m (any order gives the same maximum)
+    float m = -INFINITY;
+    for (int sp = c; sp < n_splits; sp += D) m = fmaxf(m, base_p[sp * stride + D]);
+    red_s[c] = m;
+    __syncthreads();
+    if (c == 0) {
         float M = -INFINITY;
-        for (int s = 0; s < n_splits; ++s) M = fmaxf(M, base_p[s * stride + D]);
-        float Ls = 0.0f, A = 0.0f;
-        for (int s = 0; s < n_splits; ++s) {
-            const float *pp = base_p + s * stride;
-            const float cw = exp2_diff(pp[D], M);
-            Ls += pp[D + 1] * cw;
-            A += pp[c] * cw;
-        }
-        out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
+        for (int i = 0; i < D; ++i) M = fmaxf(M, red_s[i]);
+        ML_s[0] = M;
     }
+    __syncthreads();
+    const float M = ML_s[0];
+    for (int sp = c; sp < n_splits; sp += D) cw_s[sp] = exp2_diff(base_p[sp * stride + D], M);
+    __syncthreads();
+    if (c == 0) {
+        float Ls = 0.0f;
+        for (int sp = 0; sp < n_splits; ++sp) Ls += base_p[sp * stride + D + 1] * cw_s[sp];
+        ML_s[1] = Ls;
+    }
+    constexpr int kBatch = 8;
+    float A = 0.0f;
+    for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
+        float v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            v[u] = s0 + u < n_splits ? base_p[(int64_t)(s0 + u) * stride + c] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (s0 + u < n_splits) A += v[u] * cw_s[s0 + u];
+    }
+    __syncthreads();
+    const float Ls = ML_s[1];
+    out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
 }
 
 int env_int(const char *name, int dflt) {
@@ -140,8 +168,8 @@ int launch_t(const rkv_gqa &g, int B, const void *q, const rkv_paged_cache &c,
     }
     int st = launch_status();
     if (st != RKV_OK || pl.n_splits == 1) return st;
-    attend_merge_kernel<D, G><<<dim3(g.n_kv_heads, B), 256, 0, s>>>(g.n_kv_heads, pl.n_splits,
-                                                                   a.part, out);
+    attend_merge_kernel<D, G><<<dim3(g.n_kv_heads, B, G), D, 0, s>>>(g.n_kv_heads, pl.n_splits,
+                                                                     a.part, out);
     return launch_status();
 }
 
