@@ -159,6 +159,44 @@ int rkv_prefill_evict(const rkv_gqa *g, int32_t dtype, int32_t B,
                       float *pooled_scores, int32_t *seq_lens_out, void *ws,
                       size_t ws_bytes, void *stream);
 
+/* ---- chunked-prefill eviction -------------------------------------------- */
+/* [P3] "Evidence": stage-1 eviction re-enforces its budget across the calls
+ * of a chunked prefill.  Each call evicts over the sequence formed by the
+ * n_cached[b] rows already in the cache (logical rows 0 .. n_cached-1, in
+ * order) followed by the chunk_lens[b] rows of the new chunk, exactly as
+ * rkv_prefill_evict does for a prompt of L = n_cached + chunk_len rows whose
+ * observation window is the chunk's last w queries; the kept rows end up in
+ * logical rows [0, min(keep, L)) of the cache and the summaries are rebuilt
+ * for them.  kept_idx and pooled_scores index that concatenated sequence.
+ *
+ * Arguments (as rkv_prefill_evict unless noted)
+ *   n_cached      : host [B], rows now in the cache (>= 0).
+ *   chunk_lens    : host [B], rows in this chunk; chunk_len >= w unless
+ *                   n_cached + chunk_len <= keep (nothing to evict).
+ *   C_max         : row stride of k_chunk/v_chunk, >= every chunk_len.
+ *   q_win         : device [B][Hq][w][d], the chunk's last w queries.
+ *   k_chunk, v_chunk : device [B][Hkv][C_max][d], 16-byte aligned.
+ *   cache         : holds the n_cached rows (n_cached <= max_pages * P);
+ *                   needs min(keep, L) <= max_pages * P; its rows are read,
+ *                   then rewritten.
+ *   pooled_scores : device [B][Hkv][L_max] fp32, optional, with
+ *                   L_max = max_b (n_cached + chunk_len).
+ *   ws, ws_bytes  : device workspace of at least
+ *                   rkv_prefill_evict_chunk_workspace_bytes(g, B, L_max, w)
+ *                   for that L_max.
+ * Errors: RKV_EINVAL, RKV_EUNSUPPORTED, RKV_ECAPACITY, RKV_EWORKSPACE,
+ * RKV_EHIP. */
+size_t rkv_prefill_evict_chunk_workspace_bytes(const rkv_gqa *g, int32_t B, int64_t L_max,
+                                               int32_t w);
+int rkv_prefill_evict_chunk(const rkv_gqa *g, int32_t dtype, int32_t B,
+                            const int32_t *n_cached, const int32_t *chunk_lens,
+                            const int32_t *keep, int64_t C_max, int32_t w,
+                            int32_t pool_kernel, float scale, const void *q_win,
+                            const void *k_chunk, const void *v_chunk,
+                            const rkv_paged_cache *cache, void *summaries, int32_t *kept_idx,
+                            int32_t keep_stride, float *pooled_scores, int32_t *seq_lens_out,
+                            void *ws, size_t ws_bytes, void *stream);
+
 /* ---- incremental page-summary append ------------------------------------ */
 /* [P3] "Where it sits" (paged max/min) and "Evidence" (incremental update
  * == rebuild).  For every sequence b, rows [n_old[b], n_new[b]) are folded

@@ -155,6 +155,30 @@ def snapkv_group(q_win: np.ndarray, k: np.ndarray, pool_kernel: int, keep: int,
     return kept[:keep_eff], A[:npre], pooled[:npre]
 
 
+def snapkv_chunked_group(q_wins, k_chunks, pool_kernel: int, keeps, scale: float):
+    """SnapKV++ across the calls of a chunked prefill, for one KV head group
+    ("RocketKV-adapted -- Two-Stage Compression", "Evidence": the stage-1
+    budget is re-enforced across chunked-prefill calls).  Reading: call t
+    appends chunk t (keys k_chunks[t] [C_t, d]) to the rows kept so far and
+    applies snapkv_group to that concatenation with the chunk's last w
+    queries q_wins[t] [G, w, d] and budget keeps[t].
+    Returns one (kept, pooled, kept_positions) per call: kept indexes the
+    concatenation, kept_positions are original prompt positions."""
+    rows = np.asarray(k_chunks[0])[:0]
+    pos = np.zeros(0, np.int64)
+    off = 0
+    out = []
+    for q, kc, keep in zip(q_wins, k_chunks, keeps):
+        kc = np.asarray(kc)
+        cat = np.concatenate([rows, kc])
+        cpos = np.concatenate([pos, off + np.arange(len(kc), dtype=np.int64)])
+        off += len(kc)
+        kept, _, pooled = snapkv_group(q, cat, pool_kernel, keep, scale)
+        rows, pos = cat[kept], cpos[kept]
+        out.append((kept, pooled, pos.copy()))
+    return out
+
+
 def hsa_group(q: np.ndarray, k: np.ndarray, v: np.ndarray, smax: np.ndarray,
               smin: np.ndarray, n: int, P: int, k1: int, k2: int, scale: float):
     """HSA decode for one KV head group.  q [G, d]; k, v [>=n, d]; summaries

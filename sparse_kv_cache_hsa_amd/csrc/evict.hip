@@ -527,7 +527,85 @@ int launch_t(const rkv_gqa &g, int B, const EvictSeq &seq, int64_t L_max, int w,
     return RKV_OK;
 }
 
+// Chunked prefill: logical rows [0, n_cached) from the paged cache followed
+// by the chunk's rows, copied into one contiguous [B][Hkv][L_max][d] buffer
+// that the eviction pipeline then reads like a prompt.
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+concat_kernel(int Hkv, int64_t L_max, ChunkSeq cs, const T *k_chunk, const T *v_chunk,
+              int64_t C_max, const T *k_pool, const T *v_pool, const int32_t *page_table,
+              int P, int max_pages, int64_t num_blocks, T *k_cat, T *v_cat) {
+    constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+    constexpr int RPB = 256 / CPR;
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
+    const int chunk = threadIdx.x % CPR;
+    if (row >= cs.L[b]) return;
+    const int64_t bh = (int64_t)b * Hkv + h;
+    uint4 kx = make_uint4(0u, 0u, 0u, 0u), vx = kx;
+    if (row < cs.n_cached[b]) {
+        const int32_t blk = page_table[(int64_t)b * max_pages + row / P];
+        if (blk >= 0 && blk < num_blocks) {
+            const int64_t src = (((int64_t)blk * Hkv + h) * P + row % P) * D;
+            kx = ((const uint4 *)(k_pool + src))[chunk];
+            vx = ((const uint4 *)(v_pool + src))[chunk];
+        }
+    } else {
+        const int64_t src = (bh * C_max + (row - cs.n_cached[b])) * D;
+        kx = ((const uint4 *)(k_chunk + src))[chunk];
+        vx = ((const uint4 *)(v_chunk + src))[chunk];
+    }
+    const int64_t dst = (bh * L_max + row) * D;
+    ((uint4 *)(k_cat + dst))[chunk] = kx;
+    ((uint4 *)(v_cat + dst))[chunk] = vx;
+}
+
+template <typename T, int D>
+void launch_concat(const rkv_gqa &g, int B, const ChunkSeq &cs, int64_t L_max,
+                   const void *k_chunk, const void *v_chunk, int64_t C_max,
+                   const rkv_paged_cache &c, void *k_cat, void *v_cat, hipStream_t s) {
+    constexpr int RPB = 256 / (D * (int)sizeof(T) / 16);
+    concat_kernel<T, D><<<dim3((int)((L_max + RPB - 1) / RPB), g.n_kv_heads, B), 256, 0, s>>>(
+        g.n_kv_heads, L_max, cs, (const T *)k_chunk, (const T *)v_chunk, C_max,
+        (const T *)c.k_pool, (const T *)c.v_pool, c.page_table, c.page_size, c.max_pages,
+        c.num_blocks, (T *)k_cat, (T *)v_cat);
+}
+
+size_t cat_bytes(const rkv_gqa &g, int B, int64_t L_max) {
+    // sized for 4-byte elements, so it serves either element type
+    return align_up((size_t)B * g.n_kv_heads * L_max * g.head_dim * 4);
+}
+
 }  // namespace
+
+size_t evict_chunk_ws_bytes(const rkv_gqa &g, int B, int64_t L_max, int w) {
+    return 2 * cat_bytes(g, B, L_max) + evict_ws_bytes(g, B, L_max, w);
+}
+
+int launch_evict_chunk(const rkv_gqa &g, int dtype, int B, const ChunkSeq &cs, const EvictSeq &seq,
+                       int64_t L_max, int64_t C_max, int w, int pool_kernel, float scale,
+                       const void *q_win, const void *k_chunk, const void *v_chunk,
+                       const rkv_paged_cache &c, void *summaries, int32_t *kept_idx,
+                       int keep_stride, float *pooled, int32_t *seq_lens_out, void *ws,
+                       hipStream_t s) {
+    char *base = (char *)ws;
+    void *k_cat = base, *v_cat = base + cat_bytes(g, B, L_max);
+    void *ews = base + 2 * cat_bytes(g, B, L_max);
+    const int d = g.head_dim;
+    if (dtype == RKV_F32) {
+        if (d == 64) launch_concat<float, 64>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, s);
+        else if (d == 128) launch_concat<float, 128>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, s);
+        else return RKV_EUNSUPPORTED;
+    } else {
+        if (d == 64) launch_concat<uint16_t, 64>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, s);
+        else if (d == 128) launch_concat<uint16_t, 128>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, s);
+        else return RKV_EUNSUPPORTED;
+    }
+    const int st = launch_status();
+    if (st != RKV_OK) return st;
+    return launch_evict(g, dtype, B, seq, L_max, w, pool_kernel, scale, q_win, k_cat, v_cat, c,
+                        summaries, kept_idx, keep_stride, pooled, seq_lens_out, ews, s);
+}
 
 size_t evict_ws_bytes(const rkv_gqa &g, int B, int64_t L_max, int w) {
     return evict_layout(g, B, L_max, w).total;

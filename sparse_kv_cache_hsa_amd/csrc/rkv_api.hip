@@ -130,6 +130,62 @@ int rkv_prefill_evict(const rkv_gqa *g, int32_t dtype, int32_t B, const int32_t 
                         (hipStream_t)stream);
 }
 
+size_t rkv_prefill_evict_chunk_workspace_bytes(const rkv_gqa *g, int32_t B, int64_t L_max,
+                                               int32_t w) {
+    if (check_gqa(g) != RKV_OK || B < 1 || L_max < 1 || w < 1) return 0;
+    return evict_chunk_ws_bytes(*g, B, L_max, w);
+}
+
+int rkv_prefill_evict_chunk(const rkv_gqa *g, int32_t dtype, int32_t B,
+                            const int32_t *n_cached, const int32_t *chunk_lens,
+                            const int32_t *keep, int64_t C_max, int32_t w,
+                            int32_t pool_kernel, float scale, const void *q_win,
+                            const void *k_chunk, const void *v_chunk,
+                            const rkv_paged_cache *cache, void *summaries, int32_t *kept_idx,
+                            int32_t keep_stride, float *pooled_scores, int32_t *seq_lens_out,
+                            void *ws, size_t ws_bytes, void *stream) {
+    int st = check_gqa(g);
+    if (st != RKV_OK) return st;
+    if ((st = check_dtype(dtype)) != RKV_OK) return st;
+    if (B < 1 || !n_cached || !chunk_lens || !keep || !q_win || !k_chunk || !v_chunk)
+        return RKV_EINVAL;
+    if (B > RKV_MAX_EVICT_BATCH) return RKV_EUNSUPPORTED;
+    if (C_max < 1 || C_max > ((int64_t)1 << 30) || w < 1 || pool_kernel < 1 ||
+        (pool_kernel % 2) == 0)
+        return RKV_EINVAL;
+    if (!(scale > 0.0f) || !isfinite(scale)) return RKV_EINVAL;
+    if (!aligned16(k_chunk) || !aligned16(v_chunk)) return RKV_EINVAL;
+    if ((st = check_cache(cache)) != RKV_OK) return st;
+    const int64_t cap = (int64_t)cache->max_pages * cache->page_size;
+    ChunkSeq cs;
+    EvictSeq seq;
+    memset(&cs, 0, sizeof cs);
+    memset(&seq, 0, sizeof seq);
+    int64_t L_max = 1, keep_rows = 0;
+    for (int b = 0; b < B; ++b) {
+        const int32_t nc = n_cached[b], cl = chunk_lens[b], kp = keep[b];
+        if (nc < 0 || cl < 0 || cl > C_max || kp < 0) return RKV_EINVAL;
+        if (nc > cap) return RKV_ECAPACITY;
+        const int64_t L = (int64_t)nc + cl;
+        if (L > 0x7fffffff) return RKV_EINVAL;
+        if (kp < L && (kp < w || cl < w)) return RKV_EINVAL;
+        const int64_t ke = kp < L ? kp : L;
+        if (ke > cap) return RKV_ECAPACITY;
+        if (ke > keep_rows) keep_rows = ke;
+        if (L > L_max) L_max = L;
+        cs.n_cached[b] = nc;
+        cs.L[b] = (int32_t)L;
+        seq.L[b] = (int32_t)L;
+        seq.keep[b] = kp;
+    }
+    if (kept_idx && keep_stride < keep_rows) return RKV_EINVAL;
+    const size_t need = evict_chunk_ws_bytes(*g, B, L_max, w);
+    if (!ws || ws_bytes < need) return RKV_EWORKSPACE;
+    return launch_evict_chunk(*g, dtype, B, cs, seq, L_max, C_max, w, pool_kernel, scale, q_win,
+                              k_chunk, v_chunk, *cache, summaries, kept_idx, keep_stride,
+                              pooled_scores, seq_lens_out, ws, (hipStream_t)stream);
+}
+
 int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,
                          const rkv_paged_cache *cache, const int32_t *n_old,
                          const int32_t *n_new, int32_t max_new_rows, const void *k_src,

@@ -308,6 +308,17 @@ struct EvictSeq {
     int32_t keep[RKV_MAX_EVICT_BATCH];
 };
 size_t evict_ws_bytes(const rkv_gqa &g, int B, int64_t L_max, int w);
+struct ChunkSeq {
+    int32_t n_cached[RKV_MAX_EVICT_BATCH];
+    int32_t L[RKV_MAX_EVICT_BATCH];  // n_cached + chunk_len
+};
+size_t evict_chunk_ws_bytes(const rkv_gqa &g, int B, int64_t L_max, int w);
+int launch_evict_chunk(const rkv_gqa &g, int dtype, int B, const ChunkSeq &cs, const EvictSeq &seq,
+                       int64_t L_max, int64_t C_max, int w, int pool_kernel, float scale,
+                       const void *q_win, const void *k_chunk, const void *v_chunk,
+                       const rkv_paged_cache &c, void *summaries, int32_t *kept_idx,
+                       int keep_stride, float *pooled, int32_t *seq_lens_out, void *ws,
+                       hipStream_t s);
 int launch_evict(const rkv_gqa &g, int dtype, int B, const EvictSeq &seq, int64_t L_max,
                  int w, int pool_kernel, float scale, const void *q_win, const void *k,
                  const void *v, const rkv_paged_cache &c, void *summaries,

@@ -33,7 +33,7 @@ EXPORTED = (
     "rkv_status_string", "rkv_build_id", "rkv_split_ratio",
     "rkv_prefill_evict_workspace_bytes", "rkv_prefill_evict", "rkv_append_summaries",
     "rkv_hsa_workspace_bytes", "rkv_hsa_select", "rkv_hsa_attend", "rkv_hsa_decode",
-    "rkv_decode_step",
+    "rkv_decode_step", "rkv_prefill_evict_chunk_workspace_bytes", "rkv_prefill_evict_chunk",
 )
 
 
@@ -83,6 +83,12 @@ def load_library(path: str | None = None, check_build_id: bool = True):
         lib.rkv_prefill_evict.argtypes = [G, i32, i32, P(i32), P(i32), i64, i32, i32, f32, vp,
                                           vp, vp, C, vp, vp, i32, vp, vp, vp, sz, vp]
         lib.rkv_prefill_evict.restype = ctypes.c_int
+        lib.rkv_prefill_evict_chunk_workspace_bytes.argtypes = [G, i32, i64, i32]
+        lib.rkv_prefill_evict_chunk_workspace_bytes.restype = sz
+        lib.rkv_prefill_evict_chunk.argtypes = [G, i32, i32, P(i32), P(i32), P(i32), i64, i32,
+                                                i32, f32, vp, vp, vp, C, vp, vp, i32, vp, vp,
+                                                vp, sz, vp]
+        lib.rkv_prefill_evict_chunk.restype = ctypes.c_int
         lib.rkv_append_summaries.argtypes = [G, i32, i32, C, vp, vp, i32, vp, vp, vp, vp]
         lib.rkv_append_summaries.restype = ctypes.c_int
         lib.rkv_hsa_workspace_bytes.argtypes = [G, i32, i32, i32, i32, i32]
@@ -231,6 +237,49 @@ def rkv_prefill_evict(g: rkv_gqa, prompt_lens, keep, q_win: torch.Tensor, k: tor
         float(scale), q_win.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(cs),
         _ptr(summaries), _ptr(kept_idx), stride, _ptr(pooled_scores), _ptr(seq_lens_out),
         ws.data_ptr(), ws.numel(), _stream()))
+
+
+def rkv_prefill_evict_chunk_workspace_bytes(g: rkv_gqa, B: int, L_max: int, w: int) -> int:
+    return int(load_library().rkv_prefill_evict_chunk_workspace_bytes(ctypes.byref(g), B, L_max,
+                                                                      w))
+
+
+def rkv_prefill_evict_chunk(g: rkv_gqa, n_cached, chunk_lens, keep, q_win: torch.Tensor,
+                            k_chunk: torch.Tensor, v_chunk: torch.Tensor, w: int,
+                            pool_kernel: int, scale: float, cache: PagedCache,
+                            summaries: torch.Tensor | None = None,
+                            kept_idx: torch.Tensor | None = None,
+                            pooled_scores: torch.Tensor | None = None,
+                            seq_lens_out: torch.Tensor | None = None,
+                            ws: torch.Tensor | None = None) -> None:
+    """SnapKV++ eviction over the cached rows followed by a prefill chunk.
+    n_cached/chunk_lens/keep: host sequences of ints (length B); q_win
+    [B, Hq, w, d] (the chunk's last w queries); k_chunk, v_chunk
+    [B, Hkv, C_max, d].  kept_idx and pooled_scores index the concatenated
+    sequence; pooled_scores is [B, Hkv, max(n_cached + chunk_lens)]."""
+    _need(k_chunk, "k_chunk")
+    _need(v_chunk, "v_chunk", k_chunk.dtype)
+    _need(q_win, "q_win", k_chunk.dtype)
+    _need(summaries, "summaries", k_chunk.dtype, optional=True)
+    _need(kept_idx, "kept_idx", torch.int32, optional=True)
+    _need(pooled_scores, "pooled_scores", torch.float32, optional=True)
+    _need(seq_lens_out, "seq_lens_out", torch.int32, optional=True)
+    B, C_max = int(k_chunk.shape[0]), int(k_chunk.shape[2])
+    nc = (ctypes.c_int32 * B)(*[int(x) for x in n_cached])
+    cl = (ctypes.c_int32 * B)(*[int(x) for x in chunk_lens])
+    keeps = (ctypes.c_int32 * B)(*[int(x) for x in keep])
+    L_max = max(1, max(int(a) + int(c) for a, c in zip(n_cached, chunk_lens)))
+    if ws is None:
+        ws = torch.empty(rkv_prefill_evict_chunk_workspace_bytes(g, B, L_max, w),
+                         dtype=torch.uint8, device=k_chunk.device)
+    _need(ws, "ws")
+    cs = cache.c_struct()
+    stride = int(kept_idx.shape[-1]) if kept_idx is not None else 0
+    _check("rkv_prefill_evict_chunk", load_library().rkv_prefill_evict_chunk(
+        ctypes.byref(g), _dtype_code(k_chunk), B, nc, cl, keeps, C_max, int(w),
+        int(pool_kernel), float(scale), q_win.data_ptr(), k_chunk.data_ptr(),
+        v_chunk.data_ptr(), ctypes.byref(cs), _ptr(summaries), _ptr(kept_idx), stride,
+        _ptr(pooled_scores), _ptr(seq_lens_out), ws.data_ptr(), ws.numel(), _stream()))
 
 
 def rkv_append_summaries(g: rkv_gqa, cache: PagedCache, n_old: torch.Tensor,

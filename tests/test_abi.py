@@ -111,3 +111,25 @@ def test_evict_argument_checks(rkv_lib):
     assert call([50], [20], stride=10) == L.RKV_EINVAL       # kept_idx row too short
     assert call([50], [20], ws=100) == L.RKV_EWORKSPACE
     assert call([50] * 200, [20] * 200) == L.RKV_EUNSUPPORTED  # batch above the limit
+
+
+def test_evict_chunk_argument_checks(rkv_lib):
+    L = rkv_lib
+    lib = L.load_library()
+    g = L.gqa(2, 2, 64)
+    fake = 0x10000
+    cache = L.rkv_paged_cache(fake, fake, fake, 64, 16, 4)
+
+    def call(n_cached, chunks, keeps, w=8, C_max=100, ws=1 << 30):
+        B = len(chunks)
+        arr = lambda xs: (ctypes.c_int32 * B)(*xs)
+        return lib.rkv_prefill_evict_chunk(
+            ctypes.byref(g), 0, B, arr(n_cached), arr(chunks), arr(keeps), C_max, w, 7, 0.125,
+            fake, fake, fake, ctypes.byref(cache), None, None, 0, None, None, fake, ws, None)
+
+    assert call([40], [30], [20], w=40) == L.RKV_EINVAL     # evicting with a chunk below w
+    assert call([40], [120], [20]) == L.RKV_EINVAL          # chunk longer than C_max
+    assert call([-1], [30], [20]) == L.RKV_EINVAL           # negative row count
+    assert call([70], [30], [20]) == L.RKV_ECAPACITY        # 70 cached rows > 4 pages x 16
+    assert call([40], [30], [20], ws=100) == L.RKV_EWORKSPACE
+    assert lib.rkv_prefill_evict_chunk_workspace_bytes(ctypes.byref(g), 1, 70, 8) > 0

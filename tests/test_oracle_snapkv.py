@@ -125,3 +125,58 @@ def test_invalid_arguments():
         oracle.snapkv_group(q, k, 4, 20, 0.3)        # even pooling kernel
     with pytest.raises(oracle.OracleError):
         oracle.snapkv_group(q, k, 3, 5, 0.3)         # keep below the window
+
+
+# ---- chunked prefill (the budget re-enforced across calls) ------------------
+def _chunks(G, w, d, lens, seed, dtype=torch.float32):
+    qs, ks = [], []
+    for t, n in enumerate(lens):
+        q, k = make(G, w, n, d, seed + t, dtype)
+        qs.append(q)
+        ks.append(k)
+    return qs, ks
+
+
+def test_chunked_single_chunk_is_plain_eviction():
+    qs, ks = _chunks(4, 8, 32, [400], 71)
+    (kept, pooled, pos), = oracle.snapkv_chunked_group(qs, ks, 7, [100], 0.2)
+    k2, _, p2 = oracle.snapkv_group(qs[0], ks[0], 7, 100, 0.2)
+    np.testing.assert_array_equal(kept, k2)
+    np.testing.assert_array_equal(pos, k2)
+    np.testing.assert_array_equal(pooled, p2)
+
+
+def test_chunked_budget_window_and_order():
+    """After every call: min(keep, rows so far + chunk) rows kept, positions
+    ascending, the chunk's last w rows kept, earlier positions only from rows
+    kept before (evicted rows never come back)."""
+    w, lens, keeps = 8, [300, 120, 500, 90], [150, 150, 200, 120]
+    qs, ks = _chunks(2, w, 32, lens, 81)
+    res = oracle.snapkv_chunked_group(qs, ks, 5, keeps, 0.2)
+    held, start = set(), 0
+    for (kept, _, pos), n, keep in zip(res, lens, keeps):
+        L = len(held) + n
+        assert len(pos) == min(keep, L)
+        assert np.all(np.diff(pos) > 0)
+        end = start + n
+        assert set(range(end - w, end)) <= set(pos.tolist())
+        assert set(p for p in pos.tolist() if p < start) <= held
+        held, start = set(pos.tolist()), end
+
+
+def test_chunked_without_pressure_keeps_everything():
+    lens = [50, 60, 70]
+    qs, ks = _chunks(1, 4, 16, lens, 91)
+    res = oracle.snapkv_chunked_group(qs, ks, 3, [1000] * 3, 0.25)
+    np.testing.assert_array_equal(res[-1][2], np.arange(sum(lens)))
+
+
+def test_chunked_second_call_scores_the_concatenation():
+    """Call 2 scores exactly the kept rows of call 1 followed by chunk 2,
+    against the window of chunk 2 (fp64 causal softmax reference)."""
+    G, w, d = 2, 8, 32
+    qs, ks = _chunks(G, w, d, [200, 100], 101)
+    res = oracle.snapkv_chunked_group(qs, ks, 1, [80, 90], 0.2)
+    cat = np.concatenate([ks[0][res[0][0]], ks[1]])
+    ref = reference_scores(qs[1], cat, 0.2)
+    np.testing.assert_allclose(res[1][1], ref, rtol=2e-5, atol=1e-9)
