@@ -85,12 +85,17 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     T *sm_max = summ + bh * 2 * D * max_pages;
     T *sm_min = sm_max + (int64_t)D * max_pages;
 
-    // 1. the loads that do not depend on the row count: the new K/V row and
-    //    the queries (they share a memory round trip with the row count).
     const bool append = k_new != nullptr && n > 0;
     const int p_new = append ? (int)((n - 1) / P) : -1;
     const int slot = append ? (int)(n - 1 - (int64_t)p_new * P) : 0;
     const int64_t im = (int64_t)tid * max_pages + p_new;
+    const int K = min(k2, NP);
+    constexpr int V = 16 / (int)sizeof(T);
+    const bool staged = (size_t)2 * k1 * ((NP + V - 1) / V * V) * sizeof(T) <= kStageBytes &&
+                        NP <= kBlock;
+
+    // 1. the loads that do not depend on the row count: the new K/V row and
+    //    the queries (they share a memory round trip with the row count).
     T x{}, vx{};
     if (k_new != nullptr && tid < D) {
         x = k_new[bh * D + tid];
@@ -100,21 +105,28 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     load_group_q<T, D, G, kBlock>(q, bh, qs);
     lds_barrier();
 
-    // 2. channels
+    // 2. channels.  The page-table row and the appended page's old summary
+    //    (which depend on the row count) are loaded into registers
+    //    meanwhile.
+    int32_t pt = 0;
+    T omax{}, omin{};
+    if (staged) {
+        if (tid < NP) pt = a.page_table[(int64_t)b * max_pages + tid];
+        if (append && tid < D && slot != 0) {
+            omax = sm_max[im];
+            omin = sm_min[im];
+        }
+    }
     rank_channels<D, G, kBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot,
                                 kPacked ? qpm_s : nullptr);
     if (a.chan_out && tid < k1) a.chan_out[bh * k1 + tid] = ch_s[tid];
 
-    // 3. the second memory round trip: the page-table row, the appended
-    //    page's old summary and, when they fit, the summaries of the chosen
-    //    channels; then the appended row is folded in (first of equal values
-    //    kept: strict comparisons, as in a rebuild) and stored.  The page
-    //    holding the appended row is scored from LDS with its new summary.
+    // 3. the appended row is folded into its page's summary (first of equal
+    //    values kept: strict comparisons, as in a rebuild) and stored; when
+    //    they fit, the summaries of the chosen channels are copied to LDS
+    //    (the second memory round trip) and the appended page's column is
+    //    replaced there by its new summary.
     // 4. page bounds and page top-k2.
-    const int K = min(k2, NP);
-    constexpr int V = 16 / (int)sizeof(T);
-    const bool staged = (size_t)2 * k1 * ((NP + V - 1) / V * V) * sizeof(T) <= kStageBytes &&
-                        NP <= kBlock;
     auto emit = [&](int o, int i) { sel_s[o] = i; };
     auto fold = [&](T xv, T omax, T omin, T &nmax, T &nmin) {
         nmax = xv;
@@ -135,34 +147,21 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             sm_min[im] = nmin;
         }
     };
-    T omax{}, omin{};
     if (staged) {
-        dma_copy_i32<kBlock>(a.page_table + (int64_t)b * max_pages, NP, blk_s);
-        T cx{}, comax{}, comin{};
-        if (append && tid < D && slot != 0) {
-            omax = sm_max[im];
-            omin = sm_min[im];
-        }
-        if (append && tid < k1) {
-            const int c = ch_s[tid];
-            cx = xs[c];
-            if (slot != 0) {
-                comax = sm_max[(int64_t)c * max_pages + p_new];
-                comin = sm_min[(int64_t)c * max_pages + p_new];
-            }
-        }
         const int npad = stage_summaries<T, kBlock>(sm_max, sm_min, max_pages, 0, NP, ch_s, k1, stage);
-        lds_barrier();
-        if (append && tid < k1) {
-            T nmax, nmin;
-            fold(cx, comax, comin, nmax, nmin);
-            stage[(int64_t)tid * npad + p_new] = nmax;
-            stage[(int64_t)(k1 + tid) * npad + p_new] = nmin;
-        }
+        if (tid < NP) blk_s[tid] = pt;
         if (append && tid < D) {
             T nmax, nmin;
             fold(x, omax, omin, nmax, nmin);
-            store_append(nmax, nmin);
+            ovr_hi[tid] = nmax;
+            ovr_lo[tid] = nmin;
+        }
+        lds_barrier();
+        if (append && tid < D) store_append(ovr_hi[tid], ovr_lo[tid]);
+        if (append && tid < k1) {
+            const int c = ch_s[tid];
+            stage[(int64_t)tid * npad + p_new] = ovr_hi[c];
+            stage[(int64_t)(k1 + tid) * npad + p_new] = ovr_lo[c];
         }
         lds_barrier();
         uint64_t key = 0;

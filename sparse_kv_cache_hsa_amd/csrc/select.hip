@@ -22,7 +22,7 @@ namespace {
 
 constexpr int kSelBlock = 256;
 constexpr int kMaxChunk = 2048;
-constexpr int kStageElems = 16384;  // 32 KB of bf16 / 64 KB of fp32 staged summaries
+constexpr int kStageBytes = 48 * 1024;  // staged summaries
 
 struct SelArgs {
     int Hkv, P, max_pages, chunk, n_chunks, k1, k2;
@@ -42,6 +42,7 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
     constexpr bool kPacked = std::is_same<T, uint16_t>::value;
     __shared__ int ch_s[D];
     __shared__ uint64_t comp_s[kMaxChunk];
+    constexpr int kStageElems = kStageBytes / (int)sizeof(T);
     __shared__ __align__(16) T stage[kStageElems];
     __shared__ int cnt_s[kSelBlock];
     __shared__ uint32_t hist[256];

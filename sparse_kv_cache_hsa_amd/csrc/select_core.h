@@ -186,7 +186,9 @@ __device__ __forceinline__ void rank_channels(const float (*qs)[D], int k1, uint
             }
         }
     };
-    if (k1 <= kWave) {
+    // Wide blocks spread the all-pairs rank count over 4+ threads per key,
+    // which beats the single-wave merge of the per-wave sorts.
+    if (k1 <= kWave && BLOCK < 4 * D) {
         topk_small<BLOCK>(key, D, k1, comp_s, emit);
     } else {
         if (tid < D) comp_s[tid] = key;
