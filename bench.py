@@ -249,12 +249,14 @@ def main():
 
     # ---- dominant kernel ----------------------------------------------------
     # Fused path: a step is one decode_kernel launch per layer on this stream,
-    # so the timed region itself gives the average launch duration.
-    # Split path: the attention launches of every layer, captured alone.
+    # so the timed region itself gives the average launch duration.  Split-K
+    # fused path: the same, per layer the split-K decode_kernel and its merge.
+    # Standalone path: the attention launches of every layer, captured alone.
     per_layer, _, n_new = inputs[W + K - 1]
-    fused = rkv.fused_path(sess.g, sess.B, sess.P, sess.max_pages, wl.k2)
-    if fused:
-        kernel = "decode_kernel"
+    mode = rkv.decode_mode(sess.g, sess.B, sess.P, sess.max_pages, wl.k2, wl.k1,
+                           rkv.RKV_BF16 if wl.dtype.itemsize == 2 else rkv.RKV_F32)
+    if mode in (1, 2):
+        kernel = "decode_kernel" if mode == 1 else "decode_kernel split-K + attend_merge_kernel"
         launch_us = ms_total * 1e3 / (K * sess.n_layers)
         bytes_launch = step_b / sess.n_layers
     else:
@@ -313,7 +315,9 @@ def main():
                    "page_size": sess.P, "k1": wl.k1, "k2": wl.k2,
                    "prompt_len_min": min(sess.prompt_lens), "prompt_len_max": max(sess.prompt_lens),
                    "kept_rows_min": min(sess.keep), "kept_rows_max": max(sess.keep),
-                   "graph": not args.no_graph, "parallelism": "single-gpu"},
+                   "graph": not args.no_graph,
+                   "path": {0: "standalone kernels", 1: "fused", 2: "fused split-K"}[mode],
+                   "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(kern_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "avg_launch_us": round(launch_us, 3),

@@ -277,10 +277,19 @@ int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
  *   k_new, v_new : device [B][Hkv][d], or both NULL (no append: this is then
  *                  rkv_hsa_decode).
  *   summaries    : current for rows [0, n-1) on entry, for [0, n) on return.
- * When the batch fills the chip (B * Hkv >= 192, G <= 4, G * d <= 512,
- * max_pages <= 2048, k2 * P <= 2048) the whole step is a single kernel, one
- * 16-wave block per (sequence, KV head); otherwise the standalone kernels run
- * in sequence.  Other arguments and errors as for rkv_hsa_decode. */
+ * How it runs (same results every way; G <= 4, G * d <= 512, max_pages <=
+ * 2048 and k2 * P <= 2048 are needed for either fused form):
+ *   - B * Hkv >= 192 (the batch fills the chip): a single kernel, one
+ *     16-wave block per (sequence, KV head);
+ *   - smaller batches whose summaries fit the kernel's LDS stage
+ *     (max_pages <= 1024 and 2 * k1 * max_pages * sizeof(element) <= 64 KiB,
+ *     max_pages rounded up to 16 bytes of elements): the same kernel split
+ *     K-wise, about 128 blocks in all, each making the unit's selection and
+ *     attending to a share of its pages, then a merge kernel (two launches);
+ *   - otherwise the standalone append, select and attention kernels.
+ * The environment variable RKV_FUSED=0/1/2 forces the standalone kernels,
+ * the one-block fused kernel or the split-K form where the shapes allow.
+ * Other arguments and errors as for rkv_hsa_decode. */
 int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                     const void *k_new, const void *v_new, const rkv_paged_cache *cache,
                     const int32_t *seq_lens, void *summaries, int32_t k1, int32_t k2,

@@ -80,41 +80,54 @@ attend_kernel(AttArgs a, const T *k_pool, const T *v_pool, const T *q) {
     }
 }
 
-// Combines the splits of one (sequence, KV head, query head of the group) in
-// split order: block (h, b, j), one thread per channel.  The split weights
-// 2^(m_s - M) are computed once into LDS; each channel then sums its split
-// partials with batches of loads in flight.
+// Combines the splits of one (sequence, KV head, query head of the group):
+// block (h, b, j), one thread per channel.  M = max of the splits' m and
+// Ls = sum of l_s 2^(m_s - M) come from wave reductions in a fixed order; the
+// split weights 2^(m_s - M) go to LDS, and each channel then sums its split
+// partials in split order with batches of loads in flight.
 constexpr int kMergeMaxSplits = 1024;
 
 template <int D, int G>
 __global__ void __launch_bounds__(D)
 attend_merge_kernel(int Hkv, int n_splits, const float *part, float *out) {
+    constexpr int NW = D / kWave;
     __shared__ float cw_s[kMergeMaxSplits];
-    __shared__ float red_s[D];
-    __shared__ float ML_s[2];
+    __shared__ float red_s[2][NW];
     const int h = blockIdx.x, b = blockIdx.y, j = blockIdx.z, c = threadIdx.x;
+    const int lane = c & (kWave - 1), w = c / kWave;
     const int64_t bh = (int64_t)b * Hkv + h;
     const int64_t stride = (int64_t)G * (D + 2);
     const float *base_p = part + (bh * n_splits * G + j) * (D + 2);
-    // M = max over the splits' m (any order gives the same maximum)
     float m = -INFINITY;
     for (int sp = c; sp < n_splits; sp += D) m = fmaxf(m, base_p[sp * stride + D]);
-    red_s[c] = m;
+    m = pair_max<1>(m);
+    m = pair_max<2>(m);
+    m = pair_max<4>(m);
+    m = pair_max<8>(m);
+    m = pair_max<16>(m);
+    m = pair_max<32>(m);
+    if (lane == 0) red_s[0][w] = m;
     __syncthreads();
-    if (c == 0) {
-        float M = -INFINITY;
-        for (int i = 0; i < D; ++i) M = fmaxf(M, red_s[i]);
-        ML_s[0] = M;
+    float M = red_s[0][0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) M = fmaxf(M, red_s[0][i]);
+    float ls = 0.0f;
+    for (int sp = c; sp < n_splits; sp += D) {
+        const float wt = exp2_diff(base_p[sp * stride + D], M);
+        cw_s[sp] = wt;
+        ls += base_p[sp * stride + D + 1] * wt;
     }
+    ls = pair_sum<1>(ls);
+    ls = pair_sum<2>(ls);
+    ls = pair_sum<4>(ls);
+    ls = pair_sum<8>(ls);
+    ls = pair_sum<16>(ls);
+    ls = pair_sum<32>(ls);
+    if (lane == 0) red_s[1][w] = ls;
     __syncthreads();
-    const float M = ML_s[0];
-    for (int sp = c; sp < n_splits; sp += D) cw_s[sp] = exp2_diff(base_p[sp * stride + D], M);
-    __syncthreads();
-    if (c == 0) {
-        float Ls = 0.0f;
-        for (int sp = 0; sp < n_splits; ++sp) Ls += base_p[sp * stride + D + 1] * cw_s[sp];
-        ML_s[1] = Ls;
-    }
+    float Ls = red_s[1][0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) Ls += red_s[1][i];
     constexpr int kBatch = 8;
     float A = 0.0f;
     for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
@@ -126,8 +139,6 @@ attend_merge_kernel(int Hkv, int n_splits, const float *part, float *out) {
         for (int u = 0; u < kBatch; ++u)
             if (s0 + u < n_splits) A += v[u] * cw_s[s0 + u];
     }
-    __syncthreads();
-    const float Ls = ML_s[1];
     out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
 }
 
@@ -228,6 +239,25 @@ size_t attend_ws_bytes(const rkv_gqa &g, int B, int P, int k2) {
     if (p.n_splits == 1) return 0;
     return align_up((size_t)B * g.n_kv_heads * p.n_splits * g.group * (g.head_dim + 2) *
                     sizeof(float));
+}
+
+int launch_attend_merge(const rkv_gqa &g, int B, int n_splits, const float *part, float *out,
+                        hipStream_t s) {
+    if (n_splits > kMergeMaxSplits) return RKV_EUNSUPPORTED;
+    const dim3 grid(g.n_kv_heads, B, g.group);
+    const int d = g.head_dim;
+    switch (g.group * 1000 + d) {
+        case 1064: attend_merge_kernel<64, 1><<<grid, 64, 0, s>>>(g.n_kv_heads, n_splits, part, out); break;
+        case 2064: attend_merge_kernel<64, 2><<<grid, 64, 0, s>>>(g.n_kv_heads, n_splits, part, out); break;
+        case 4064: attend_merge_kernel<64, 4><<<grid, 64, 0, s>>>(g.n_kv_heads, n_splits, part, out); break;
+        case 8064: attend_merge_kernel<64, 8><<<grid, 64, 0, s>>>(g.n_kv_heads, n_splits, part, out); break;
+        case 1128: attend_merge_kernel<128, 1><<<grid, 128, 0, s>>>(g.n_kv_heads, n_splits, part, out); break;
+        case 2128: attend_merge_kernel<128, 2><<<grid, 128, 0, s>>>(g.n_kv_heads, n_splits, part, out); break;
+        case 4128: attend_merge_kernel<128, 4><<<grid, 128, 0, s>>>(g.n_kv_heads, n_splits, part, out); break;
+        case 8128: attend_merge_kernel<128, 8><<<grid, 128, 0, s>>>(g.n_kv_heads, n_splits, part, out); break;
+        default: return RKV_EUNSUPPORTED;
+    }
+    return launch_status();
 }
 
 int launch_attend(const rkv_gqa &g, int dtype, int B, const void *q, const rkv_paged_cache &c,

@@ -14,8 +14,13 @@
 // streaming core (attend_core.h).
 //
 // Used when the batch fills the chip (enough (sequence, head) units for
-// every CU) and the shapes fit LDS; otherwise the standalone append, select
-// and split-K attention kernels run in sequence.
+// every CU) and the shapes fit LDS.  For smaller batches the split-K variant
+// runs S blocks per unit: every block makes the same selection (the unit's
+// summaries are small and stay in L2), streams 1/S of the selected pages and
+// writes a partial (max, sum, acc) that the attention merge kernel combines
+// in split order; block 0 of a unit writes the appended row, the summary and
+// the index outputs.  Two launches per step instead of five.  Otherwise the
+// standalone append, select and attention kernels run in sequence.
 #include <stdlib.h>
 
 #include <type_traits>
@@ -31,6 +36,7 @@ constexpr int kBlock = kNW * kWave;
 constexpr int kFusedMaxPages = 2048;
 constexpr int kFusedMaxRows = 2048;
 constexpr size_t kStageBytes = 64 * 1024;
+constexpr int kSplitBlocks = 128;
 
 constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
 
@@ -42,9 +48,11 @@ struct DecArgs {
     float *out;
     int32_t *chan_out, *page_out;
     float *score_out;
+    float *part;  // split-K: [B][Hkv][n_splits][G][D + 2] partials
+    int pps;      // split-K: selected pages per split
 };
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool SPLIT>
 __global__ void __launch_bounds__(kBlock)
 decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, T *v_pool,
               T *summ) {
@@ -76,7 +84,10 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     // still read the row table
     __shared__ typename Core::Shared csh;
 
-    const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+    const int sp = SPLIT ? blockIdx.x : 0, nsp = SPLIT ? gridDim.x : 1;
+    const int h = SPLIT ? blockIdx.y : blockIdx.x, b = SPLIT ? blockIdx.z : blockIdx.y;
+    const int tid = threadIdx.x;
+    const bool lead = sp == 0;  // writes the append and the index outputs
     const int P = a.P, k1 = a.k1, k2 = a.k2, max_pages = a.max_pages;
     const int64_t bh = (int64_t)b * a.Hkv + h;
     const int64_t cap = (int64_t)max_pages * P;
@@ -119,7 +130,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     }
     rank_channels<D, G, kBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot,
                                 kPacked ? qpm_s : nullptr);
-    if (a.chan_out && tid < k1) a.chan_out[bh * k1 + tid] = ch_s[tid];
+    if (a.chan_out && lead && tid < k1) a.chan_out[bh * k1 + tid] = ch_s[tid];
 
     // 3. the appended row is folded into its page's summary (first of equal
     //    values kept: strict comparisons, as in a rebuild) and stored; when
@@ -139,7 +150,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     };
     auto store_append = [&](T nmax, T nmin) {
         const int32_t blk = blk_s[p_new];
-        if (blk >= 0 && blk < a.num_blocks) {
+        if (lead && blk >= 0 && blk < a.num_blocks) {
             const int64_t dst = (((int64_t)blk * a.Hkv + h) * P + slot) * D + tid;
             k_pool[dst] = x;
             v_pool[dst] = vx;
@@ -172,7 +183,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             else
                 sc = staged_bound<T, D, G>(stage, npad, tid, k1, qsel);
             key = composite_key(ordered_key(sc), tid);
-            if (a.score_out) a.score_out[bh * max_pages + tid] = sc;
+            if (a.score_out && lead) a.score_out[bh * max_pages + tid] = sc;
         }
         // the sorted keys have LDS of their own, so no barrier is needed
         // between scoring and sorting
@@ -203,7 +214,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             float sc = page_bound<T, D, G>(sm_max, sm_min, max_pages, p, ch_s, k1, qsel);
             if (p == p_new) sc = page_bound_ovr<T, D, G>(ch_s, k1, qsel, ovr_hi, ovr_lo);
             comp_s[p] = composite_key(ordered_key(sc), p);
-            if (a.score_out) a.score_out[bh * max_pages + p] = sc;
+            if (a.score_out && lead) a.score_out[bh * max_pages + p] = sc;
         }
         lds_barrier();
         topk_ascending<kBlock>(comp_s, NP, K, cnt_s, hist, sh, wave_tot, emit);
@@ -213,9 +224,11 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     // 5. resolve the rows of the selected pages, then stream them.  The full
     //    barrier makes the appended K/V row (a global store of this block)
     //    visible to every wave before any of them reads it.
-    const int nrows = K * P;
+    // (split-K: this block's share of the page list, pages [i0, i1))
+    const int i0 = SPLIT ? min(K, sp * a.pps) : 0, i1 = SPLIT ? min(K, i0 + a.pps) : K;
+    const int nrows = (i1 - i0) * P;
     for (int f = tid; f < nrows; f += kBlock) {
-        const int pi = f / P, slot = f - pi * P;
+        const int pi = i0 + f / P, slot = f - (f / P) * P;
         const int32_t pg = sel_s[pi];
         uint32_t r = kBadRow;
         if ((int64_t)pg * P + slot < n) {
@@ -224,36 +237,70 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         }
         row_s[f] = r;
     }
+    if constexpr (SPLIT) {
+        // the lead block's store of the appended row may land after this
+        // block reads it, so a block whose share holds that row writes the
+        // same bytes itself
+        if (!lead && append && tid < D) {
+            bool mine = false;
+            for (int pi = i0; pi < i1; ++pi) mine |= sel_s[pi] == p_new;
+            const int32_t blk = blk_s[p_new];
+            if (mine && blk >= 0 && blk < a.num_blocks) {
+                const int64_t dst = (((int64_t)blk * a.Hkv + h) * P + slot) * D + tid;
+                k_pool[dst] = x;
+                v_pool[dst] = vx;
+            }
+        }
+    }
     Core core;
     core.init_lds(qs, a.qscale);
     __syncthreads();
     core.stream(row_s, nrows, k_pool, v_pool);
     core.to_shared(csh);
     lds_barrier();
-    Core::combine(csh, [&](int j, int c, float M, float Ls, float A) {
-        a.out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
-    });
+    if constexpr (SPLIT) {
+        float *base = a.part + (bh * nsp + sp) * G * (D + 2);
+        Core::combine(csh, [&](int j, int c, float M, float Ls, float A) {
+            float *pp = base + j * (D + 2);
+            pp[c] = A;
+            if (c == 0) {
+                pp[D] = M;
+                pp[D + 1] = Ls;
+            }
+        });
+    } else {
+        Core::combine(csh, [&](int j, int c, float M, float Ls, float A) {
+            a.out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
+        });
+    }
     // the page list goes out last: stored earlier, it would hold up the full
     // barrier before the stream (which waits for this wave's stores)
-    if (a.page_out)
+    if (a.page_out && lead)
         for (int o = tid; o < k2; o += kBlock) a.page_out[bh * k2 + o] = o < K ? sel_s[o] : -1;
 }
 
 template <typename T, int D, int G>
-void launch_t(int B, const rkv_gqa &g, const DecArgs &a, const void *q, const void *k_new,
-              const void *v_new, const rkv_paged_cache &c, void *summ, hipStream_t s) {
-    decode_kernel<T, D, G><<<dim3(g.n_kv_heads, B), kBlock, 0, s>>>(
-        a, (const T *)q, (const T *)k_new, (const T *)v_new, (T *)c.k_pool, (T *)c.v_pool,
-        (T *)summ);
+void launch_t(int B, int nsp, const rkv_gqa &g, const DecArgs &a, const void *q,
+              const void *k_new, const void *v_new, const rkv_paged_cache &c, void *summ,
+              hipStream_t s) {
+    if (nsp > 0)
+        decode_kernel<T, D, G, true><<<dim3(nsp, g.n_kv_heads, B), kBlock, 0, s>>>(
+            a, (const T *)q, (const T *)k_new, (const T *)v_new, (T *)c.k_pool, (T *)c.v_pool,
+            (T *)summ);
+    else
+        decode_kernel<T, D, G, false><<<dim3(g.n_kv_heads, B), kBlock, 0, s>>>(
+            a, (const T *)q, (const T *)k_new, (const T *)v_new, (T *)c.k_pool, (T *)c.v_pool,
+            (T *)summ);
 }
 
 template <typename T, int D>
-bool dispatch_g(int B, const rkv_gqa &g, const DecArgs &a, const void *q, const void *k_new,
-                const void *v_new, const rkv_paged_cache &c, void *summ, hipStream_t s) {
+bool dispatch_g(int B, int nsp, const rkv_gqa &g, const DecArgs &a, const void *q,
+                const void *k_new, const void *v_new, const rkv_paged_cache &c, void *summ,
+                hipStream_t s) {
     switch (g.group) {
-        case 1: launch_t<T, D, 1>(B, g, a, q, k_new, v_new, c, summ, s); return true;
-        case 2: launch_t<T, D, 2>(B, g, a, q, k_new, v_new, c, summ, s); return true;
-        case 4: launch_t<T, D, 4>(B, g, a, q, k_new, v_new, c, summ, s); return true;
+        case 1: launch_t<T, D, 1>(B, nsp, g, a, q, k_new, v_new, c, summ, s); return true;
+        case 2: launch_t<T, D, 2>(B, nsp, g, a, q, k_new, v_new, c, summ, s); return true;
+        case 4: launch_t<T, D, 4>(B, nsp, g, a, q, k_new, v_new, c, summ, s); return true;
     }
     return false;
 }
@@ -263,22 +310,51 @@ int env_int(const char *name, int dflt) {
     return (v && *v) ? atoi(v) : dflt;
 }
 
-}  // namespace
-
-bool fused_decode_ok(const rkv_gqa &g, int B, int P, int max_pages, int k2) {
-    if (g.group * g.head_dim > 512 || g.group > 4) return false;
-    if (max_pages > kFusedMaxPages || (int64_t)k2 * P > kFusedMaxRows) return false;
-    const int force = env_int("RKV_FUSED", -1);
-    if (force == 0) return false;
-    if (force == 1) return true;
-    return B * g.n_kv_heads >= 192;
+// Split-K shape: about kSplitBlocks blocks in all, whole pages per split.
+void split_counts(int units, int k2, int &n_splits, int &pages_per_split) {
+    const int target = env_int("RKV_SPLITK_BLOCKS", kSplitBlocks);
+    int want = (target + units - 1) / units;
+    if (want > k2) want = k2;
+    if (want < 1) want = 1;
+    pages_per_split = (k2 + want - 1) / want;
+    n_splits = (k2 + pages_per_split - 1) / pages_per_split;
 }
 
-int launch_decode_fused(const rkv_gqa &g, int dtype, int B, const void *q, const void *k_new,
-                        const void *v_new, const rkv_paged_cache &c, const int32_t *seq_lens,
-                        void *summaries, int k1, int k2, float scale, float *out,
-                        int32_t *chan_idx, int32_t *page_idx, float *page_scores,
-                        hipStream_t s) {
+}  // namespace
+
+FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, int k1, int k2) {
+    FusedPlan p{0, 0, 0};
+    if (g.group * g.head_dim > 512 || g.group > 4) return p;
+    if (max_pages > kFusedMaxPages || (int64_t)k2 * P > kFusedMaxRows) return p;
+    const int units = B * g.n_kv_heads;
+    // split-K needs the staged selection (every page's summaries in LDS),
+    // else each of its blocks would read the summaries from memory
+    const int esz = dtype == RKV_F32 ? 4 : 2, V = 16 / esz;
+    const bool stage_fits = max_pages <= kBlock &&
+        (int64_t)2 * k1 * ((max_pages + V - 1) / V * V) * esz <= (int64_t)kStageBytes;
+    int mode = units >= 192 ? 1 : (stage_fits ? 2 : 0);
+    const int force = env_int("RKV_FUSED", -1);
+    if (force == 0 || force == 1) mode = force;
+    else if (force == 2 && stage_fits) mode = 2;
+    p.mode = mode;
+    if (mode == 2) split_counts(units, k2, p.n_splits, p.pages_per_split);
+    return p;
+}
+
+size_t fused_split_ws_bytes(const rkv_gqa &g, int B, int k2) {
+    // the split-K plan's partials for any dtype, k1 and RKV_FUSED setting:
+    // the same split count as plan_fused, whatever the batch
+    const int units = B * g.n_kv_heads;
+    int nsp, pps;
+    split_counts(units, k2, nsp, pps);
+    return align_up((size_t)units * nsp * g.group * (g.head_dim + 2) * sizeof(float));
+}
+
+int launch_decode_fused(const FusedPlan &pl, const rkv_gqa &g, int dtype, int B, const void *q,
+                        const void *k_new, const void *v_new, const rkv_paged_cache &c,
+                        const int32_t *seq_lens, void *summaries, int k1, int k2, float scale,
+                        float *out, int32_t *chan_idx, int32_t *page_idx, float *page_scores,
+                        float *part, size_t part_bytes, hipStream_t s) {
     DecArgs a;
     a.Hkv = g.n_kv_heads;
     a.P = c.page_size;
@@ -293,17 +369,25 @@ int launch_decode_fused(const rkv_gqa &g, int dtype, int B, const void *q, const
     a.chan_out = chan_idx;
     a.page_out = page_idx;
     a.score_out = page_scores;
+    a.part = part;
+    a.pps = pl.pages_per_split;
+    const int nsp = pl.mode == 2 ? pl.n_splits : 0;
+    if (nsp > 0 && (!part || (size_t)B * g.n_kv_heads * nsp * g.group * (g.head_dim + 2) *
+                                     sizeof(float) > part_bytes))
+        return RKV_EWORKSPACE;
     bool ok = false;
     const int d = g.head_dim;
     if (dtype == RKV_F32) {
-        if (d == 64) ok = dispatch_g<float, 64>(B, g, a, q, k_new, v_new, c, summaries, s);
-        else if (d == 128) ok = dispatch_g<float, 128>(B, g, a, q, k_new, v_new, c, summaries, s);
+        if (d == 64) ok = dispatch_g<float, 64>(B, nsp, g, a, q, k_new, v_new, c, summaries, s);
+        else if (d == 128) ok = dispatch_g<float, 128>(B, nsp, g, a, q, k_new, v_new, c, summaries, s);
     } else {
-        if (d == 64) ok = dispatch_g<uint16_t, 64>(B, g, a, q, k_new, v_new, c, summaries, s);
-        else if (d == 128) ok = dispatch_g<uint16_t, 128>(B, g, a, q, k_new, v_new, c, summaries, s);
+        if (d == 64) ok = dispatch_g<uint16_t, 64>(B, nsp, g, a, q, k_new, v_new, c, summaries, s);
+        else if (d == 128) ok = dispatch_g<uint16_t, 128>(B, nsp, g, a, q, k_new, v_new, c, summaries, s);
     }
     if (!ok) return RKV_EUNSUPPORTED;
-    return launch_status();
+    const int st = launch_status();
+    if (st != RKV_OK || nsp == 0) return st;
+    return launch_attend_merge(g, B, nsp, part, out, s);
 }
 
 }  // namespace rkv

@@ -211,7 +211,8 @@ size_t rkv_hsa_workspace_bytes(const rkv_gqa *g, int32_t B, int32_t page_size,
     // of rkv_hsa_decode passes none; +256 so the result is never 0.
     return align_up(select_ws_bytes(*g, B, max_pages, k2)) +
            align_up(attend_ws_bytes(*g, B, page_size, k2)) +
-           align_up((size_t)B * g->n_kv_heads * k2 * sizeof(int32_t)) + 256;
+           align_up((size_t)B * g->n_kv_heads * k2 * sizeof(int32_t)) +
+           fused_split_ws_bytes(*g, B, k2) + 256;
 }
 
 int rkv_hsa_select(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
@@ -260,9 +261,15 @@ int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
     const size_t need = rkv_hsa_workspace_bytes(g, B, cache->page_size, cache->max_pages, k1, k2);
     if (!ws || ws_bytes < need) return RKV_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
-    if (fused_decode_ok(*g, B, cache->page_size, cache->max_pages, k2))
-        return launch_decode_fused(*g, dtype, B, q, k_new, v_new, *cache, seq_lens, summaries, k1,
-                                   k2, scale, out, chan_idx, page_idx, page_scores, s);
+    const FusedPlan fp = plan_fused(*g, dtype, B, cache->page_size, cache->max_pages, k1, k2);
+    if (fp.mode != 0) {
+        const size_t off = align_up(select_ws_bytes(*g, B, cache->max_pages, k2)) +
+                           align_up(attend_ws_bytes(*g, B, cache->page_size, k2)) +
+                           align_up((size_t)B * g->n_kv_heads * k2 * sizeof(int32_t));
+        return launch_decode_fused(fp, *g, dtype, B, q, k_new, v_new, *cache, seq_lens, summaries,
+                                   k1, k2, scale, out, chan_idx, page_idx, page_scores,
+                                   (float *)((char *)ws + off), ws_bytes - off, s);
+    }
     if (k_new) {
         st = launch_append(*g, dtype, B, *cache, nullptr, seq_lens, 1, k_new, v_new, summaries, s);
         if (st != RKV_OK) return st;

@@ -296,12 +296,25 @@ int launch_attend(const rkv_gqa &g, int dtype, int B, const void *q,
                   const rkv_paged_cache &c, const int32_t *seq_lens, const int32_t *page_idx,
                   int k2, float scale, float *out, void *ws, hipStream_t s);
 
-bool fused_decode_ok(const rkv_gqa &g, int B, int P, int max_pages, int k2);
-int launch_decode_fused(const rkv_gqa &g, int dtype, int B, const void *q, const void *k_new,
-                        const void *v_new, const rkv_paged_cache &c, const int32_t *seq_lens,
-                        void *summaries, int k1, int k2, float scale, float *out,
-                        int32_t *chan_idx, int32_t *page_idx, float *page_scores,
+// Combines split-K attention partials [B][Hkv][n_splits][G][d + 2] in split
+// order into out [B][Hq][d].
+int launch_attend_merge(const rkv_gqa &g, int B, int n_splits, const float *part, float *out,
                         hipStream_t s);
+
+// How rkv_decode_step runs: mode 0 = the standalone kernels, 1 = the fused
+// kernel with one block per (sequence, KV head), 2 = the fused kernel split
+// K-wise over n_splits blocks per unit (pages_per_split selected pages each)
+// plus the attention merge.
+struct FusedPlan {
+    int mode, n_splits, pages_per_split;
+};
+FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, int k1, int k2);
+size_t fused_split_ws_bytes(const rkv_gqa &g, int B, int k2);
+int launch_decode_fused(const FusedPlan &pl, const rkv_gqa &g, int dtype, int B, const void *q,
+                        const void *k_new, const void *v_new, const rkv_paged_cache &c,
+                        const int32_t *seq_lens, void *summaries, int k1, int k2, float scale,
+                        float *out, int32_t *chan_idx, int32_t *page_idx, float *page_scores,
+                        float *part, size_t part_bytes, hipStream_t s);
 
 struct EvictSeq {
     int32_t L[RKV_MAX_EVICT_BATCH];

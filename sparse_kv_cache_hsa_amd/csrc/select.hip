@@ -108,13 +108,20 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
     }
 }
 
-__global__ void __launch_bounds__(kSelBlock)
+// Top-k2 over the chunks' candidates of one (sequence, KV head): one block
+// of 1,024 threads.  The candidate keys are copied to LDS once when they fit,
+// so the four radix rounds and the ordered emit read LDS only.
+constexpr int kMergeBlock = 1024;
+constexpr int kMergeStage = 8192;  // candidate keys held in LDS
+
+__global__ void __launch_bounds__(kMergeBlock)
 merge_kernel(int Hkv, int P, int max_pages, int n_chunks, const int32_t *seq_lens, int k2,
              const uint32_t *cand_key, const int32_t *cand_page, int32_t *page_out) {
-    constexpr int NW = kSelBlock / kWave;
+    constexpr int NW = kMergeBlock / kWave;
     __shared__ uint32_t hist[256];
     __shared__ int wave_tot[NW];
     __shared__ int sh[2];
+    __shared__ uint32_t key_s[kMergeStage];
     const int b = blockIdx.y, h = blockIdx.x;
     const int64_t bh = (int64_t)b * Hkv + h;
     const int64_t cap = (int64_t)max_pages * P;
@@ -128,12 +135,20 @@ merge_kernel(int Hkv, int P, int max_pages, int n_chunks, const int32_t *seq_len
     if (K > 0) {
         uint32_t thr;
         int take_eq;
-        auto load = [&](int i) { return keys[i]; };
-        block_topk_threshold<kSelBlock>(load, m, K, hist, sh, thr, take_eq);
-        block_topk_emit<kSelBlock>(load, m, thr, take_eq, wave_tot,
-                                   [&](int o, int i) { dst[o] = pages[i]; });
+        auto emit = [&](int o, int i) { dst[o] = pages[i]; };
+        if (m <= kMergeStage) {
+            for (int i = threadIdx.x; i < m; i += kMergeBlock) key_s[i] = keys[i];
+            lds_barrier();
+            auto load = [&](int i) { return key_s[i]; };
+            block_topk_threshold<kMergeBlock>(load, m, K, hist, sh, thr, take_eq);
+            block_topk_emit<kMergeBlock>(load, m, thr, take_eq, wave_tot, emit);
+        } else {
+            auto load = [&](int i) { return keys[i]; };
+            block_topk_threshold<kMergeBlock>(load, m, K, hist, sh, thr, take_eq);
+            block_topk_emit<kMergeBlock>(load, m, thr, take_eq, wave_tot, emit);
+        }
     }
-    for (int o = K + threadIdx.x; o < k2; o += kSelBlock) dst[o] = -1;
+    for (int o = K + threadIdx.x; o < k2; o += kMergeBlock) dst[o] = -1;
 }
 
 template <typename T, int D, int G>
@@ -227,7 +242,7 @@ int launch_select(const rkv_gqa &g, int dtype, int B, const void *q, const int32
     if (!ok) return RKV_EUNSUPPORTED;
     int st = launch_status();
     if (st != RKV_OK || pl.n_chunks == 1) return st;
-    merge_kernel<<<dim3(g.n_kv_heads, B), kSelBlock, 0, s>>>(
+    merge_kernel<<<dim3(g.n_kv_heads, B), kMergeBlock, 0, s>>>(
         g.n_kv_heads, P, max_pages, pl.n_chunks, seq_lens, k2, a.cand_key, a.cand_page, page_idx);
     return launch_status();
 }

@@ -180,15 +180,31 @@ class PagedCache:
         return PagedCache(self.k_pool, self.v_pool, self.page_table[b0:b1])
 
 
-def fused_path(g: rkv_gqa, B: int, page_size: int, max_pages: int, k2: int) -> bool:
-    """Whether rkv_decode_step runs as one fused kernel for these shapes (the
-    rule documented in include/rkv.h; RKV_FUSED=0/1 overrides it)."""
-    env = os.environ.get("RKV_FUSED", "")
+def decode_mode(g: rkv_gqa, B: int, page_size: int, max_pages: int, k2: int, k1: int = 1,
+                dtype: int = RKV_BF16) -> int:
+    """How rkv_decode_step runs for these shapes (the rule documented in
+    include/rkv.h; RKV_FUSED=0/1/2 overrides it): 0 = the standalone kernels,
+    1 = one fused kernel with a block per (sequence, KV head), 2 = the fused
+    kernel split K-wise over several blocks per unit, plus the merge."""
     if g.group > 4 or g.group * g.head_dim > 512 or max_pages > 2048 or k2 * page_size > 2048:
-        return False
+        return 0
+    esz = 4 if dtype == RKV_F32 else 2
+    v = 16 // esz
+    stage_fits = max_pages <= 1024 and 2 * k1 * (-(-max_pages // v) * v) * esz <= 64 * 1024
+    mode = 1 if B * g.n_kv_heads >= 192 else (2 if stage_fits else 0)
+    env = os.environ.get("RKV_FUSED", "")
     if env in ("0", "1"):
-        return env == "1"
-    return B * g.n_kv_heads >= 192
+        mode = int(env)
+    elif env == "2" and stage_fits:
+        mode = 2
+    return mode
+
+
+def fused_path(g: rkv_gqa, B: int, page_size: int, max_pages: int, k2: int, k1: int = 1,
+               dtype: int = RKV_BF16) -> bool:
+    """Whether rkv_decode_step runs as the fused kernel with one block per
+    (sequence, KV head)."""
+    return decode_mode(g, B, page_size, max_pages, k2, k1, dtype) == 1
 
 
 # ---- entry points (same names as the C ABI) ---------------------------------

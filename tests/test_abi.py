@@ -83,7 +83,20 @@ def test_workspace_sizes(rkv_lib):
     g = L.gqa(8, 4, 128)
     a = L.rkv_hsa_workspace_bytes(g, 1, 16, 256, 32, 32)
     b = L.rkv_hsa_workspace_bytes(g, 32, 16, 400, 32, 64)
-    assert 0 < a <= b
+    assert a > 0 and b > 0
+    # batch 1 (8 units) runs the split-K fused kernel: 16 splits of two pages,
+    # each a (max, sum, acc[128]) partial per query head in fp32
+    assert a >= 8 * 16 * 4 * (128 + 2) * 4
+    # the split-K partials fit for every batch, also where the default rule
+    # picks another path (RKV_FUSED can force split-K there)
+    for (Hkv, G, d, B, k2) in [(8, 4, 128, 24, 64), (8, 4, 128, 32, 64), (8, 4, 128, 1, 32),
+                               (2, 4, 64, 1, 16), (1, 4, 128, 200, 1024), (3, 1, 64, 4, 7)]:
+        units = B * Hkv
+        want = min(k2, -(-128 // units))
+        pps = -(-k2 // want)
+        nsp = -(-k2 // pps)
+        need = units * nsp * G * (d + 2) * 4
+        assert L.rkv_hsa_workspace_bytes(L.gqa(Hkv, G, d), B, 16, 400, 32, k2) >= need
     e1 = L.rkv_prefill_evict_workspace_bytes(g, 1, 32768, 32)
     # logits for 128 window rows over 32K keys dominate: 4 B each
     assert e1 >= 8 * 32768 * 128 * 4

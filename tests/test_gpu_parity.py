@@ -99,14 +99,24 @@ def run_decode_case(case, seed, q_override=None, k_override=None, mode="decode")
     return worst, out
 
 
-@pytest.fixture(params=["auto", "fused", "split"])
+@pytest.fixture(params=["auto", "fused", "splitk", "split"])
 def path(request, monkeypatch):
-    """Which implementation rkv_hsa_decode / rkv_decode_step dispatch to."""
-    if request.param == "fused":
-        monkeypatch.setenv("RKV_FUSED", "1")
-    elif request.param == "split":
-        monkeypatch.setenv("RKV_FUSED", "0")
+    """Which implementation rkv_hsa_decode / rkv_decode_step dispatch to:
+    the default rule, the fused kernel with one block per unit, the fused
+    kernel split K-wise (plus the merge), or the standalone kernels."""
+    env = {"fused": "1", "splitk": "2", "split": "0"}.get(request.param)
+    if env is not None:
+        monkeypatch.setenv("RKV_FUSED", env)
     return request.param
+
+
+def case_mode(case):
+    """The decode mode the library picks for a case under the current
+    RKV_FUSED setting."""
+    dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages = case
+    rkv = lib()
+    return rkv.decode_mode(rkv.gqa(Hkv, G, d), B, P, max_pages, k2, k1,
+                           rkv.RKV_F32 if dtype == F32 else rkv.RKV_BF16)
 
 
 def fused_supported(case):
@@ -120,6 +130,8 @@ def test_decode_matches_oracle(ci, mode, path):
     case = DECODE_CASES[ci]
     if path == "fused" and not fused_supported(case):
         pytest.skip("shape outside the fused kernel's limits (dispatches to the split path)")
+    if path == "splitk" and case_mode(case) != 2:
+        pytest.skip("shape outside the split-K fused kernel's limits")
     run_decode_case(case, 1000 + ci, mode=mode)
 
 
@@ -132,11 +144,13 @@ def test_decode_large_batch_default_path():
 
 
 def test_fused_and_split_select_identically(monkeypatch):
-    monkeypatch.setenv("RKV_FUSED", "1")
-    a = run_decode_case(BIG_CASE, 78, mode="step")[1].clone()
-    monkeypatch.setenv("RKV_FUSED", "0")
-    b = run_decode_case(BIG_CASE, 78, mode="step")[1]
-    assert (a - b).abs().max().item() < 1e-5
+    outs = []
+    for env in ("1", "2", "0"):
+        monkeypatch.setenv("RKV_FUSED", env)
+        assert case_mode(BIG_CASE) == int(env)
+        outs.append(run_decode_case(BIG_CASE, 78, mode="step")[1].clone())
+    for o in outs[1:]:
+        assert (outs[0] - o).abs().max().item() < 1e-5
 
 
 def test_decode_ties_zero_query_and_identical_keys():
@@ -198,7 +212,7 @@ def test_append_in_chunks_matches_rebuild(dtype):
                        summ2.view(torch.int16 if dtype == BF16 else torch.int32))
 
 
-@pytest.mark.parametrize("fused", ["1", "0"])
+@pytest.mark.parametrize("fused", ["1", "2", "0"])
 def test_tiny_workload_decode_loop(fused, monkeypatch):
     """The tiny fp32 workload end to end: 2,048 cached rows, 32 decode steps,
     each appending its token and decoding in one rkv_decode_step call."""
@@ -320,6 +334,8 @@ def test_selection_parameterisations(name, mode, path):
     case = PARAM_CASES[name]
     if path == "fused" and not fused_supported(case):
         pytest.skip("shape outside the fused kernel's limits")
+    if path == "splitk" and case_mode(case) != 2:
+        pytest.skip("shape outside the split-K fused kernel's limits")
     run_decode_case(case, 3000 + len(name), mode=mode)
 
 
@@ -390,6 +406,8 @@ def test_random_shapes_match_oracle(ci, mode, path):
     case = RANDOM_CASES[ci]
     if path == "fused" and not fused_supported(case):
         pytest.skip("shape outside the fused kernel's limits")
+    if path == "splitk" and case_mode(case) != 2:
+        pytest.skip("shape outside the split-K fused kernel's limits")
     run_decode_case(case, 5000 + ci, mode=mode)
 
 
