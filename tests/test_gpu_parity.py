@@ -76,6 +76,16 @@ def run_decode_case(case, seed, q_override=None, k_override=None, mode="decode")
         rkv.rkv_hsa_decode(g, qd, cache, seq, summ, k1, k2, scale, out, ws, chan_idx=chan,
                            page_idx=pidx, page_scores=scores)
     torch.cuda.synchronize()
+    if mode == "step":
+        # the appended row sits in the pool at its page's block
+        for b in range(B):
+            n = lens[b]
+            if n == 0:
+                continue
+            blk = int(cache.page_table[b, (n - 1) // P])
+            for h in range(Hkv):
+                assert torch.equal(cache.k_pool[blk, h, (n - 1) % P].cpu(), K[b, h, n - 1]), (b, h)
+                assert torch.equal(cache.v_pool[blk, h, (n - 1) % P].cpu(), V[b, h, n - 1]), (b, h)
     worst = 0.0
     for b in range(B):
         n = lens[b]
@@ -137,6 +147,24 @@ def test_decode_matches_oracle(ci, mode, path):
 
 # A batch large enough for the fused kernel by default (B * Hkv >= 192).
 BIG_CASE = (BF16, 24, 8, 4, 128, 16, 32, 64, [4000 + 37 * i for i in range(24)], 320)
+
+
+def test_splitk_appended_row_read_by_a_later_split(monkeypatch):
+    """Split-K fused path, one page per split: the appended row's key points
+    along the group's queries, so its page (the highest selected index) is
+    attended by the last split, not by the block that stores the row.  The
+    output must match the oracle, and the pool must hold the new row."""
+    monkeypatch.setenv("RKV_FUSED", "2")
+    case = (BF16, 2, 2, 4, 128, 16, 32, 16, [1000, 777], 80)
+    assert case_mode(case) == 2
+    dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages = case
+    K = rand((B, Hkv, max(lens), d), 4100, dtype, 1.5)
+    q = rand((B, Hkv * G, d), 4102, dtype)
+    for b in range(B):
+        for h in range(Hkv):
+            qs = q[b, h * G:(h + 1) * G].float().sum(0)
+            K[b, h, lens[b] - 1] = (8.0 * qs / qs.norm()).to(dtype)
+    run_decode_case(case, 4100, q_override=q, k_override=K, mode="step")
 
 
 def test_decode_large_batch_default_path():
