@@ -202,9 +202,16 @@ __device__ __forceinline__ void lane_pair(uint32_t v, uint32_t &lo, uint32_t &hi
     }
 }
 
-// Value of lane (lane ^ OFF) of a 64-lane wave: DPP quad permutes for 1 and
-// 2, the lane swizzle within 32-lane halves for 4 and 8, lane swaps for 16
-// and 32.
+// Value of lane (lane ^ OFF) of a 64-lane wave, all in the vector ALU:
+//   1, 2 : one DPP quad permute ([1,0,3,2], [2,3,0,1]);
+//   4    : row half-mirror (lane i of each 8 takes lane 7-i), then the
+//          reversing quad permute [3,2,1,0]: lane l ends with lane
+//          hm(l ^ 3 within its quad) = l ^ 4;
+//   8    : row mirror (lane i of each 16 takes lane 15-i), then the half-
+//          mirror: lane l ends with lane 15 - hm(l) = l ^ 8;
+//   16, 32: the gfx950 lane swaps.
+// (DPP controls: quad_perm = the 8-bit source map, row_mirror 0x140,
+// row_half_mirror 0x141.)
 template <int OFF>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
     static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "offset");
@@ -212,12 +219,16 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
         return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, true);
     } else if constexpr (OFF == 2) {
         return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, true);
-    } else if constexpr (OFF >= 16) {
+    } else if constexpr (OFF == 4) {
+        const int h = __builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, true);
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, h, 0x1B, 0xf, 0xf, true);
+    } else if constexpr (OFF == 8) {
+        const int m = __builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, true);
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, m, 0x141, 0xf, 0xf, true);
+    } else {
         uint32_t lo, hi;
         lane_pair<OFF>(v, lo, hi);
         return (threadIdx.x & OFF) ? lo : hi;
-    } else {
-        return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (OFF << 10) | 0x1F);
     }
 }
 

@@ -71,8 +71,8 @@ __device__ __forceinline__ K bitonic_clean(K key, int lane) {
 }
 
 // Sorts the 64 keys of a wave in descending order (lane i gets the i-th
-// largest).  Distances 1 and 2 move through DPP, 4 to 16 through the lane
-// swizzle, 32 through a permute.
+// largest).  Distances 1 to 8 move through DPP (one or two lane moves),
+// 16 and 32 through the lane swaps.
 template <typename K>
 __device__ __forceinline__ K wave_sort_desc(K key) {
     const int lane = threadIdx.x & (kWave - 1);
