@@ -26,8 +26,8 @@ def _short(name: str) -> str:
     return name if len(name) <= 60 else name[:57] + "..."
 
 
-def stats_table(path: str, top: int = 12) -> str:
-    rows = list(csv.DictReader(open(path)))
+def stats_table(path: str, top: int = 12, match: str = "") -> str:
+    rows = [r for r in csv.DictReader(open(path)) if match in r["Name"]]
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     out = [f"{'kernel':52s} {'calls':>7s} {'avg us':>10s} {'min us':>9s} {'max us':>9s} {'share':>7s}"]
     for r in rows[:top]:
@@ -86,6 +86,7 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("--top", type=int, default=12)
+    s.add_argument("--match", default="", help="only kernels whose name contains this")
     c = sub.add_parser("counters")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -98,7 +99,7 @@ def main(argv=None):
     c.add_argument("--commands", nargs="+", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
-        print(stats_table(a.csv, a.top))
+        print(stats_table(a.csv, a.top, a.match))
         return
     res = counters(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes, a.kernel)
     res = {"build_id": a.build_id, "workload": a.workload, **res, "commands": a.commands}
