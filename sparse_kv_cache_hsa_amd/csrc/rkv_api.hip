@@ -225,8 +225,9 @@ int rkv_hsa_select(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
     if (!summaries || !page_idx) return RKV_EINVAL;
     if (!ws || ws_bytes < rkv_hsa_workspace_bytes(g, B, page_size, max_pages, k1, k2))
         return RKV_EWORKSPACE;
-    return launch_select(*g, dtype, B, q, seq_lens, page_size, max_pages, summaries, k1, k2,
-                         chan_idx, page_idx, page_scores, ws, (hipStream_t)stream);
+    return launch_select(*g, dtype, B, q, seq_lens, page_size, max_pages, (void *)summaries, k1,
+                         k2, chan_idx, page_idx, page_scores, ws, nullptr, nullptr, nullptr,
+                         (hipStream_t)stream);
 }
 
 int rkv_hsa_attend(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
@@ -270,16 +271,13 @@ int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                                    k1, k2, scale, out, chan_idx, page_idx, page_scores,
                                    (float *)((char *)ws + off), ws_bytes - off, s);
     }
-    if (k_new) {
-        st = launch_append(*g, dtype, B, *cache, nullptr, seq_lens, 1, k_new, v_new, summaries, s);
-        if (st != RKV_OK) return st;
-    }
     if (!page_idx) {
         page_idx = (int32_t *)((char *)ws + align_up(select_ws_bytes(*g, B, cache->max_pages, k2)) +
                                align_up(attend_ws_bytes(*g, B, cache->page_size, k2)));
     }
+    // the select kernel appends the new token itself
     st = launch_select(*g, dtype, B, q, seq_lens, cache->page_size, cache->max_pages, summaries,
-                       k1, k2, chan_idx, page_idx, page_scores, ws, s);
+                       k1, k2, chan_idx, page_idx, page_scores, ws, k_new, v_new, cache, s);
     if (st != RKV_OK) return st;
     char *base = (char *)ws + align_up(select_ws_bytes(*g, B, cache->max_pages, k2));
     return launch_attend(*g, dtype, B, q, *cache, seq_lens, page_idx, k2, scale, out, base, s);

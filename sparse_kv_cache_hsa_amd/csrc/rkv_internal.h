@@ -290,9 +290,12 @@ struct SelectPlan {
 };
 SelectPlan plan_select(const rkv_gqa &g, int B, int max_pages, int k2);
 size_t select_ws_bytes(const rkv_gqa &g, int B, int max_pages, int k2);
+// With k_new/v_new and cache given (a decode step), the block whose chunk
+// holds row n-1 also appends it: K/V row into the cache, page summary folded.
 int launch_select(const rkv_gqa &g, int dtype, int B, const void *q, const int32_t *seq_lens,
-                  int P, int max_pages, const void *summaries, int k1, int k2,
+                  int P, int max_pages, void *summaries, int k1, int k2,
                   int32_t *chan_idx, int32_t *page_idx, float *page_scores, void *ws,
+                  const void *k_new, const void *v_new, const rkv_paged_cache *cache,
                   hipStream_t s);
 
 struct AttendPlan {

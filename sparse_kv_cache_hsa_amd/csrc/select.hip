@@ -7,7 +7,10 @@
 //                   channels (cheap, repeated per chunk), scores one chunk of
 //                   pages (one thread per page, coalesced along the page axis)
 //                   and keeps the chunk's top k2.  With one chunk it writes
-//                   page_idx directly.
+//                   page_idx directly.  For a decode step it also appends the
+//                   new token: the block whose chunk holds row n-1 writes the
+//                   K/V row, folds it into that page's summary and scores the
+//                   page from the new summary (no other block reads it).
 //   merge_kernel  : grid (Hkv, B).  Top-k2 over the chunks' candidates, which
 //                   are stored chunk-major in ascending page order, so the
 //                   position order equals the page order for tie-breaking.
@@ -27,6 +30,11 @@ constexpr int kStageBytes = 48 * 1024;  // staged summaries
 struct SelArgs {
     int Hkv, P, max_pages, chunk, n_chunks, k1, k2;
     const int32_t *seq_lens;
+    // decode-step append (k_new == nullptr: none)
+    const void *k_new, *v_new;
+    void *k_pool, *v_pool;
+    const int32_t *page_table;
+    int64_t num_blocks;
     int32_t *chan_out, *page_out;
     float *score_out;
     uint32_t *cand_key;
@@ -34,13 +42,14 @@ struct SelArgs {
 };
 
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q, const T *summ) {
+__global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q, T *summ) {
     constexpr int NW = kSelBlock / kWave;
     __shared__ float qs[G][D];
     __shared__ float qsel[G][D];
     __shared__ __align__(16) float qpm_s[D * 2 * G];
     constexpr bool kPacked = std::is_same<T, uint16_t>::value;
     __shared__ int ch_s[D];
+    __shared__ T ovr_hi[D], ovr_lo[D];
     __shared__ uint64_t comp_s[kMaxChunk];
     constexpr int kStageElems = kStageBytes / (int)sizeof(T);
     __shared__ __align__(16) T stage[kStageElems];
@@ -56,20 +65,52 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
     const int64_t n = min<int64_t>(max<int64_t>(a.seq_lens[b], 0), cap);
     const int NP = (int)((n + P - 1) / P);
 
+    const int p0 = ck * a.chunk;
+    const int cnt = max(0, min(NP, p0 + a.chunk) - p0);
+    T *smax = summ + bh * 2 * D * a.max_pages;
+    T *smin = smax + (int64_t)D * a.max_pages;
+    // the append, when this chunk holds row n-1 (first of equal values kept:
+    // strict comparisons, as in a rebuild)
+    const int p_new = (a.k_new && n > 0) ? (int)((n - 1) / P) : -1;
+    const bool app = p_new >= p0 && p_new < p0 + cnt;
+    if (app && tid < D) {
+        const int slot = (int)(n - 1 - (int64_t)p_new * P);
+        const int64_t im = (int64_t)tid * a.max_pages + p_new;
+        const T x = ((const T *)a.k_new)[bh * D + tid];
+        T nmax = x, nmin = x;
+        if (slot != 0) {
+            const T omax = smax[im], omin = smin[im];
+            const float fx = Elem<T>::ld(&x, 0);
+            nmax = fx > Elem<T>::ld(&omax, 0) ? x : omax;
+            nmin = fx < Elem<T>::ld(&omin, 0) ? x : omin;
+        }
+        ovr_hi[tid] = nmax;
+        ovr_lo[tid] = nmin;
+        const int32_t blk = a.page_table[(int64_t)b * a.max_pages + p_new];
+        if (blk >= 0 && blk < a.num_blocks) {
+            const int64_t dst = (((int64_t)blk * a.Hkv + h) * P + slot) * D + tid;
+            ((T *)a.k_pool)[dst] = x;
+            ((T *)a.v_pool)[dst] = ((const T *)a.v_new)[bh * D + tid];
+            smax[im] = nmax;
+            smin[im] = nmin;
+        }
+    }
     load_group_q<T, D, G, kSelBlock>(q, bh, qs);
     lds_barrier();
     rank_channels<D, G, kSelBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot,
                                        kPacked ? qpm_s : nullptr);
     if (a.chan_out && ck == 0 && tid < k1) a.chan_out[bh * k1 + tid] = ch_s[tid];
-
-    const int p0 = ck * a.chunk;
-    const int cnt = max(0, min(NP, p0 + a.chunk) - p0);
-    const T *smax = summ + bh * 2 * D * a.max_pages;
-    const T *smin = smax + (int64_t)D * a.max_pages;
     constexpr int V = 16 / (int)sizeof(T);
     if (2 * k1 * ((cnt + V - 1) / V * V) <= kStageElems) {
         const int npad = stage_summaries<T, kSelBlock>(smax, smin, a.max_pages, p0, cnt, ch_s, k1,
                                                        stage);
+        lds_barrier();
+        if (app && tid < k1) {
+            const int c = ch_s[tid];
+            const int pi = p_new - p0;
+            stage[(int64_t)tid * npad + pi] = ovr_hi[c];
+            stage[(int64_t)(k1 + tid) * npad + pi] = ovr_lo[c];
+        }
         lds_barrier();
         for (int pi = tid; pi < cnt; pi += kSelBlock) {
             float s;
@@ -82,7 +123,9 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
         }
     } else {
         for (int pi = tid; pi < cnt; pi += kSelBlock) {
-            const float s = page_bound<T, D, G>(smax, smin, a.max_pages, p0 + pi, ch_s, k1, qsel);
+            const float s = app && p0 + pi == p_new
+                                ? page_bound_ovr<T, D, G>(ch_s, k1, qsel, ovr_hi, ovr_lo)
+                                : page_bound<T, D, G>(smax, smin, a.max_pages, p0 + pi, ch_s, k1, qsel);
             comp_s[pi] = composite_key(ordered_key(s), pi);
             if (a.score_out) a.score_out[bh * a.max_pages + p0 + pi] = s;
         }
@@ -152,13 +195,12 @@ merge_kernel(int Hkv, int P, int max_pages, int n_chunks, const int32_t *seq_len
 }
 
 template <typename T, int D, int G>
-void launch_t(dim3 grid, hipStream_t s, const SelArgs &a, const void *q, const void *summ) {
-    select_kernel<T, D, G><<<grid, kSelBlock, 0, s>>>(a, (const T *)q, (const T *)summ);
+void launch_t(dim3 grid, hipStream_t s, const SelArgs &a, const void *q, void *summ) {
+    select_kernel<T, D, G><<<grid, kSelBlock, 0, s>>>(a, (const T *)q, (T *)summ);
 }
 
 template <typename T, int D>
-bool dispatch_g(int G, dim3 grid, hipStream_t s, const SelArgs &a, const void *q,
-                const void *summ) {
+bool dispatch_g(int G, dim3 grid, hipStream_t s, const SelArgs &a, const void *q, void *summ) {
     switch (G) {
         case 1: launch_t<T, D, 1>(grid, s, a, q, summ); return true;
         case 2: launch_t<T, D, 2>(grid, s, a, q, summ); return true;
@@ -206,8 +248,9 @@ size_t select_ws_bytes(const rkv_gqa &g, int B, int max_pages, int k2) {
 }
 
 int launch_select(const rkv_gqa &g, int dtype, int B, const void *q, const int32_t *seq_lens,
-                  int P, int max_pages, const void *summaries, int k1, int k2,
+                  int P, int max_pages, void *summaries, int k1, int k2,
                   int32_t *chan_idx, int32_t *page_idx, float *page_scores, void *ws,
+                  const void *k_new, const void *v_new, const rkv_paged_cache *cache,
                   hipStream_t s) {
     const SelectPlan pl = plan_select(g, B, max_pages, k2);
     SelArgs a;
@@ -224,6 +267,12 @@ int launch_select(const rkv_gqa &g, int dtype, int B, const void *q, const int32
     a.score_out = page_scores;
     a.cand_key = nullptr;
     a.cand_page = nullptr;
+    a.k_new = cache ? k_new : nullptr;
+    a.v_new = v_new;
+    a.k_pool = cache ? cache->k_pool : nullptr;
+    a.v_pool = cache ? cache->v_pool : nullptr;
+    a.page_table = cache ? cache->page_table : nullptr;
+    a.num_blocks = cache ? cache->num_blocks : 0;
     if (pl.n_chunks > 1) {
         const size_t m = (size_t)B * g.n_kv_heads * pl.n_chunks * k2;
         a.cand_key = (uint32_t *)ws;
