@@ -69,8 +69,10 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
     const int cnt = max(0, min(NP, p0 + a.chunk) - p0);
     T *smax = summ + bh * 2 * D * a.max_pages;
     T *smin = smax + (int64_t)D * a.max_pages;
+    load_group_q<T, D, G, kSelBlock>(q, bh, qs);
     // the append, when this chunk holds row n-1 (first of equal values kept:
-    // strict comparisons, as in a rebuild)
+    // strict comparisons, as in a rebuild); after the query loads, which its
+    // stores would otherwise hold back
     const int p_new = (a.k_new && n > 0) ? (int)((n - 1) / P) : -1;
     const bool app = p_new >= p0 && p_new < p0 + cnt;
     if (app && tid < D) {
@@ -95,7 +97,6 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
             smin[im] = nmin;
         }
     }
-    load_group_q<T, D, G, kSelBlock>(q, bh, qs);
     lds_barrier();
     rank_channels<D, G, kSelBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot,
                                        kPacked ? qpm_s : nullptr);
