@@ -247,7 +247,9 @@ int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,
  *   ws, ws_bytes : device workspace of at least rkv_hsa_workspace_bytes(...)
  *                  for the same shapes; calls sharing one workspace must be
  *                  ordered on one stream.
- * rkv_hsa_decode = rkv_hsa_select followed by rkv_hsa_attend on `stream`.
+ * rkv_hsa_decode gives the results of rkv_hsa_select followed by
+ * rkv_hsa_attend on `stream`; it runs as rkv_decode_step without an append
+ * (one of the fused forms where the shapes allow).
  * Errors: RKV_EINVAL, RKV_EUNSUPPORTED, RKV_EWORKSPACE, RKV_EHIP. */
 size_t rkv_hsa_workspace_bytes(const rkv_gqa *g, int32_t B, int32_t page_size,
                                int32_t max_pages, int32_t k1, int32_t k2);

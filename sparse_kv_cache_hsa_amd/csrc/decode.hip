@@ -9,7 +9,7 @@
 // chosen channels, page scores and page list never leave LDS, and the block's
 // attention phase starts as soon as its own selection is done, so a layer
 // costs one launch and one dependent chain of memory round trips instead of
-// three kernels.  Selection uses the same device code as the standalone
+// a chain of kernels.  Selection uses the same device code as the standalone
 // kernels (select_core.h), so its bits are identical; attention uses the
 // streaming core (attend_core.h).
 //
@@ -19,8 +19,9 @@
 // summaries are small and stay in L2), streams 1/S of the selected pages and
 // writes a partial (max, sum, acc) that the attention merge kernel combines
 // in split order; block 0 of a unit writes the appended row, the summary and
-// the index outputs.  Two launches per step instead of five.  Otherwise the
-// standalone append, select and attention kernels run in sequence.
+// the index outputs.  Two launches per step instead of four.  Otherwise the
+// standalone select (which appends the token) and attention kernels run in
+// sequence.
 #include <stdlib.h>
 
 #include <type_traits>
