@@ -292,6 +292,14 @@ int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
  * The environment variable RKV_FUSED=0/1/2 forces the standalone kernels,
  * the one-block fused kernel or the split-K form where the shapes allow.
  * Other arguments and errors as for rkv_hsa_decode. */
+/* Which form rkv_decode_step (and rkv_hsa_decode) takes for these shapes,
+ * by the rule above and the current RKV_FUSED setting: 0 = the standalone
+ * kernels, 1 = the fused kernel with one block per (sequence, KV head),
+ * 2 = the fused kernel split K-wise plus the merge.  Host only, no device
+ * work.  Errors: RKV_EINVAL (bad layout or sizes), RKV_EUNSUPPORTED (dtype). */
+int rkv_decode_mode(const rkv_gqa *g, int32_t dtype, int32_t B, int32_t page_size,
+                    int32_t max_pages, int32_t k1, int32_t k2);
+
 int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                     const void *k_new, const void *v_new, const rkv_paged_cache *cache,
                     const int32_t *seq_lens, void *summaries, int32_t k1, int32_t k2,

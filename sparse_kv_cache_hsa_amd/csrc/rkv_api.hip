@@ -247,6 +247,17 @@ int rkv_hsa_attend(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                          (hipStream_t)stream);
 }
 
+int rkv_decode_mode(const rkv_gqa *g, int32_t dtype, int32_t B, int32_t page_size,
+                    int32_t max_pages, int32_t k1, int32_t k2) {
+    int st = check_gqa(g);
+    if (st != RKV_OK) return st;
+    if (dtype != RKV_F32 && dtype != RKV_BF16) return RKV_EUNSUPPORTED;
+    if (B < 1 || page_size < 1 || max_pages < 1 || k1 < 1 || k1 > g->head_dim || k2 < 1 ||
+        k2 > RKV_MAX_K2)
+        return RKV_EINVAL;
+    return plan_fused(*g, dtype, B, page_size, max_pages, k1, k2).mode;
+}
+
 int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                     const void *k_new, const void *v_new, const rkv_paged_cache *cache,
                     const int32_t *seq_lens, void *summaries, int32_t k1, int32_t k2,

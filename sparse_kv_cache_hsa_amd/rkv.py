@@ -34,6 +34,7 @@ EXPORTED = (
     "rkv_prefill_evict_workspace_bytes", "rkv_prefill_evict", "rkv_append_summaries",
     "rkv_hsa_workspace_bytes", "rkv_hsa_select", "rkv_hsa_attend", "rkv_hsa_decode",
     "rkv_decode_step", "rkv_prefill_evict_chunk_workspace_bytes", "rkv_prefill_evict_chunk",
+    "rkv_decode_mode",
 )
 
 
@@ -93,6 +94,8 @@ def load_library(path: str | None = None, check_build_id: bool = True):
         lib.rkv_append_summaries.restype = ctypes.c_int
         lib.rkv_hsa_workspace_bytes.argtypes = [G, i32, i32, i32, i32, i32]
         lib.rkv_hsa_workspace_bytes.restype = sz
+        lib.rkv_decode_mode.argtypes = [G, i32, i32, i32, i32, i32, i32]
+        lib.rkv_decode_mode.restype = ctypes.c_int
         lib.rkv_hsa_select.argtypes = [G, i32, i32, vp, vp, i32, i32, vp, i32, i32, vp, vp, vp,
                                        vp, sz, vp]
         lib.rkv_hsa_select.restype = ctypes.c_int
@@ -182,21 +185,14 @@ class PagedCache:
 
 def decode_mode(g: rkv_gqa, B: int, page_size: int, max_pages: int, k2: int, k1: int = 1,
                 dtype: int = RKV_BF16) -> int:
-    """How rkv_decode_step runs for these shapes (the rule documented in
-    include/rkv.h; RKV_FUSED=0/1/2 overrides it): 0 = the standalone kernels,
-    1 = one fused kernel with a block per (sequence, KV head), 2 = the fused
-    kernel split K-wise over several blocks per unit, plus the merge."""
-    if g.group > 4 or g.group * g.head_dim > 512 or max_pages > 2048 or k2 * page_size > 2048:
-        return 0
-    esz = 4 if dtype == RKV_F32 else 2
-    v = 16 // esz
-    stage_fits = max_pages <= 1024 and 2 * k1 * (-(-max_pages // v) * v) * esz <= 64 * 1024
-    mode = 1 if B * g.n_kv_heads >= 192 else (2 if stage_fits else 0)
-    env = os.environ.get("RKV_FUSED", "")
-    if env in ("0", "1"):
-        mode = int(env)
-    elif env == "2" and stage_fits:
-        mode = 2
+    """How rkv_decode_step runs for these shapes (rkv_decode_mode: the rule
+    documented in include/rkv.h, RKV_FUSED=0/1/2 overriding it): 0 = the
+    standalone kernels, 1 = one fused kernel with a block per (sequence, KV
+    head), 2 = the fused kernel split K-wise over several blocks per unit,
+    plus the merge."""
+    mode = load_library().rkv_decode_mode(ctypes.byref(g), dtype, B, page_size, max_pages, k1, k2)
+    if mode < 0:
+        _check("rkv_decode_mode", mode)
     return mode
 
 

@@ -146,3 +146,29 @@ def test_evict_chunk_argument_checks(rkv_lib):
     assert call([70], [30], [20]) == L.RKV_ECAPACITY        # 70 cached rows > 4 pages x 16
     assert call([40], [30], [20], ws=100) == L.RKV_EWORKSPACE
     assert lib.rkv_prefill_evict_chunk_workspace_bytes(ctypes.byref(g), 1, 70, 8) > 0
+
+
+def test_decode_mode_rule(rkv_lib, monkeypatch):
+    """Which decode form runs (host-only query): the documented rule and the
+    RKV_FUSED overrides, and argument errors."""
+    L = rkv_lib
+    monkeypatch.delenv("RKV_FUSED", raising=False)
+    g = L.gqa(8, 4, 128)
+    assert L.decode_mode(g, 32, 16, 400, 64, 32) == 1      # 256 units fill the chip
+    assert L.decode_mode(g, 1, 16, 216, 32, 32) == 2       # batch 1: split-K
+    assert L.decode_mode(g, 4, 32, 4400, 128, 32) == 0     # beyond the fused page limit
+    assert L.decode_mode(g, 1, 16, 600, 32, 32) == 0       # stage too small for 600 pages
+    assert L.decode_mode(L.gqa(2, 8, 128), 1, 16, 64, 16, 16) == 0   # G > 4
+    assert L.decode_mode(L.gqa(2, 4, 64), 1, 16, 130, 16, 16, L.RKV_F32) == 2
+    monkeypatch.setenv("RKV_FUSED", "0")
+    assert L.decode_mode(g, 32, 16, 400, 64, 32) == 0
+    monkeypatch.setenv("RKV_FUSED", "2")
+    assert L.decode_mode(g, 32, 16, 400, 64, 32) == 2
+    assert L.decode_mode(g, 1, 16, 600, 32, 32) == 0       # cannot be forced past the stage
+    monkeypatch.setenv("RKV_FUSED", "1")
+    assert L.decode_mode(g, 1, 16, 216, 32, 32) == 1
+    lib = L.load_library()
+    assert lib.rkv_decode_mode(ctypes.byref(g), 1, 0, 16, 100, 8, 8) == L.RKV_EINVAL
+    assert lib.rkv_decode_mode(ctypes.byref(g), 1, 1, 16, 100, 0, 8) == L.RKV_EINVAL
+    assert lib.rkv_decode_mode(ctypes.byref(g), 7, 1, 16, 100, 8, 8) == L.RKV_EUNSUPPORTED
+    assert lib.rkv_decode_mode(None, 1, 1, 16, 100, 8, 8) == L.RKV_EINVAL
