@@ -221,17 +221,51 @@ logits_tiled_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, const T 
     }
 }
 
-__global__ void __launch_bounds__(256)
+// Row maxima from the logits kernels' per-tile maxima: one block of 1,024
+// threads per (sequence, KV head); with R <= 512 several threads share a row,
+// each over every parts-th tile with batches of loads in flight, and the
+// partial maxima meet in LDS (a maximum is exact in any order).
+constexpr int kRowMaxBlock = 1024;
+
+__global__ void __launch_bounds__(kRowMaxBlock)
 rowmax_kernel(int Hkv, int R, EvictSeq seq, int ntiles, const float *TM, float *M) {
-    const int b = blockIdx.y, h = blockIdx.x;
+    __shared__ float part_s[kRowMaxBlock];
+    const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
     const int64_t L = seq.L[b];
     if (seq.keep[b] >= L) return;
     const int64_t bh = (int64_t)b * Hkv + h;
     const int nt = (int)((L + kTK - 1) / kTK);
-    for (int r = threadIdx.x; r < R; r += 256) {
-        float m = -INFINITY;
-        for (int t = 0; t < nt; ++t) m = fmaxf(m, TM[(bh * ntiles + t) * R + r]);
-        M[bh * R + r] = m;
+    const float *tm = TM + bh * ntiles * (int64_t)R;
+    if (R > kRowMaxBlock / 2) {
+        for (int r = tid; r < R; r += kRowMaxBlock) {
+            float m = -INFINITY;
+            for (int t = 0; t < nt; ++t) m = fmaxf(m, tm[(int64_t)t * R + r]);
+            M[bh * R + r] = m;
+        }
+        return;
+    }
+    const int parts = kRowMaxBlock / R;
+    const int r = tid % R, part = tid / R;
+    float m = -INFINITY;
+    if (part < parts) {
+        constexpr int kBatch = 8;
+        for (int t0 = part; t0 < nt; t0 += parts * kBatch) {
+            float v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int t = t0 + u * parts;
+                v[u] = t < nt ? tm[(int64_t)t * R + r] : -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) m = fmaxf(m, v[u]);
+        }
+    }
+    part_s[tid] = m;
+    __syncthreads();
+    if (tid < R) {
+        float mm = part_s[tid];
+        for (int p = 1; p < parts; ++p) mm = fmaxf(mm, part_s[p * R + tid]);
+        M[bh * R + tid] = mm;
     }
 }
 
@@ -498,7 +532,7 @@ int launch_t(const rkv_gqa &g, int B, const EvictSeq &seq, int64_t L_max, int w,
         logits_kernel<T, D><<<dim3(l.ntiles, Hkv, B), kLogitsBlock, 0, s>>>(
             Hkv, R, w, L_max, seq, (const T *)q_win, (const T *)k, scale, l.ntiles, Z, TM);
     }
-    rowmax_kernel<<<dim3(Hkv, B), 256, 0, s>>>(Hkv, R, seq, l.ntiles, TM, M);
+    rowmax_kernel<<<dim3(Hkv, B), kRowMaxBlock, 0, s>>>(Hkv, R, seq, l.ntiles, TM, M);
     rowsum_kernel<<<dim3(l.nch, Hkv, B), 256, 0, s>>>(Hkv, R, w, L_max, seq, l.nch, Z, M, PL);
     rowsum_final_kernel<<<dim3(Hkv, B), 256, 0, s>>>(Hkv, R, seq, l.nch, PL, ell);
     if (R <= 128) {
