@@ -45,7 +45,7 @@ extern "C" {
 #define RKV_EINVAL (-1)       /* bad argument (null pointer, out-of-range size) */
 #define RKV_EWORKSPACE (-2)   /* workspace missing or smaller than required */
 #define RKV_ECAPACITY (-3)    /* rows do not fit the cache / page table */
-#define RKV_EUNSUPPORTED (-4) /* shape or dtype this build has no kernel for */
+#define RKV_EUNSUPPORTED (-4) /* shape or dtype the library has no kernel for */
 #define RKV_EHIP (-5)         /* a HIP launch reported an error */
 
 /* ---- element types ----------------------------------------------------- */
