@@ -10,7 +10,8 @@
 // Layout of the work inside a block of NW waves:
 //   - the block's rows are listed in an LDS table (row_s) of row units
 //     (block * Hkv + h) * P + slot, or kBadRow for rows that do not exist;
-//   - a row of d elements is read by LPR lanes with one 16-byte load each, a
+//   - a row of d elements is read by LPR lanes with one 16-byte non-temporal
+//     load each (the rows are streamed once per step), a
 //     wave reads RPW = 64/LPR rows per load and U loads of K and of V per
 //     iteration; waves take iterations round-robin;
 //   - each lane holds its EPL channels of the G query heads (the G heads share
@@ -34,6 +35,8 @@
 namespace rkv {
 
 constexpr uint32_t kBadRow = 0xffffffffu;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
 // DPP lane permutes (gfx9 encodings).
@@ -162,8 +165,12 @@ struct AttendCore {
             const uint32_t r = f < nrows ? row_s[f] : kBadRow;
             ok[u] = r != kBadRow;
             const int64_t off = (int64_t)(ok[u] ? r : 0u) * D + sub * EPL;
-            kr[u] = ok[u] ? *(const uint4 *)(k_pool + off) : make_uint4(0u, 0u, 0u, 0u);
-            vr[u] = ok[u] ? *(const uint4 *)(v_pool + off) : make_uint4(0u, 0u, 0u, 0u);
+            // every K/V row is read once per step: non-temporal loads keep
+            // the stream from displacing cached data (measurably faster)
+            const u32x4 kz = ok[u] ? __builtin_nontemporal_load((const u32x4 *)(k_pool + off)) : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 vz = ok[u] ? __builtin_nontemporal_load((const u32x4 *)(v_pool + off)) : u32x4{0u, 0u, 0u, 0u};
+            kr[u] = make_uint4(kz.x, kz.y, kz.z, kz.w);
+            vr[u] = make_uint4(vz.x, vz.y, vz.z, vz.w);
         }
     }
 

@@ -101,6 +101,26 @@ __device__ __forceinline__ int block_excl_count(bool flag, int *wave_tot, int &t
     return off + in_wave;
 }
 
+// hist[bin] += 1 for the lanes with `on`.  Keys that share their leading
+// bytes put most of a wave into one bin, and 64 LDS atomics on one address
+// serialise; so the wave first adds the lanes of the most common bins with
+// one atomic each (a ballot per distinct bin, a few rounds at most), and
+// only the lanes left over add themselves.  The counts are the same.
+__device__ __forceinline__ void wave_hist_add(uint32_t *hist, uint32_t bin, bool on) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint64_t todo = __ballot(on);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (todo == 0ull) break;
+        const int leader = __ffsll((unsigned long long)todo) - 1;
+        const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, leader);
+        const uint64_t same = __ballot(on && bin == lb) & todo;
+        if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+        todo &= ~same;
+    }
+    if ((todo >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
+}
+
 // Radix select over the keys u[0..n): finds the K-th largest key `thr`
 // (1 <= K <= n) and how many keys equal to `thr` belong to the top K
 // (`take_eq`, the lowest-indexed ones).  `hist` is LDS of 256 uint32,
@@ -115,7 +135,7 @@ __device__ void block_topk_threshold(Load load, int n, int K, uint32_t *hist, in
         lds_barrier();
         for (int i = threadIdx.x; i < n; i += BLOCK) {
             const uint32_t u = load(i);
-            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+            wave_hist_add(hist, (u >> shift) & 255u, (u & mask) == prefix);
         }
         lds_barrier();
         if (threadIdx.x < kWave) {

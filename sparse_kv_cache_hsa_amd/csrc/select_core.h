@@ -305,9 +305,11 @@ __device__ __forceinline__ void stage_rows(const T *smax, const T *smin, int max
             const int kind = row / k1, i = row - kind * k1;
             const T *src = (kind ? smin : smax) + (int64_t)ch_s[i] * max_pages + p0 + vi * E;
             // The byte count must be an int constant: a size_t expression
-            // crashes this compiler's instruction selection.
+            // crashes this compiler's instruction selection.  Cache policy
+            // 2 is the non-temporal hint: the summaries are read once per
+            // step.
             __builtin_amdgcn_global_load_lds(src, (lds_void *)(stage + (int64_t)base * E),
-                                             (int)(E * sizeof(T)), 0, 0);
+                                             (int)(E * sizeof(T)), 0, 2);
         }
     }
 }
