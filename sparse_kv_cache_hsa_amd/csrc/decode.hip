@@ -57,7 +57,7 @@ template <typename T, int D, int G, bool SPLIT>
 __global__ void __launch_bounds__(kBlock)
 decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, T *v_pool,
               T *summ) {
-    using Core = AttendCore<T, D, G, kNW, 4, false>;
+    using Core = AttendCore<T, D, G, kNW, 2, false>;
     constexpr size_t kKeyBytes = sizeof(uint64_t) * kFusedMaxPages;
     constexpr size_t kRowBytes = sizeof(uint32_t) * kFusedMaxRows;
     constexpr size_t kUnion = cmax(cmax(kStageBytes, kKeyBytes), kRowBytes);
