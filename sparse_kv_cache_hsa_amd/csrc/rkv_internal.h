@@ -307,6 +307,7 @@ int launch_append(const rkv_gqa &g, int dtype, int B, const rkv_paged_cache &c,
 struct SelectPlan {
     int chunk_pages;  // pages scored per block
     int n_chunks;     // blocks per (sequence, KV head)
+    int sorted;       // 0, or the keys per lane (1, 2, 4) of the rank-ordered list merge
 };
 SelectPlan plan_select(const rkv_gqa &g, int B, int max_pages, int k2);
 size_t select_ws_bytes(const rkv_gqa &g, int B, int max_pages, int k2);

@@ -11,9 +11,15 @@
 //                   new token: the block whose chunk holds row n-1 writes the
 //                   K/V row, folds it into that page's summary and scores the
 //                   page from the new summary (no other block reads it).
-//   merge_kernel  : grid (Hkv, B).  Top-k2 over the chunks' candidates, which
-//                   are stored chunk-major in ascending page order, so the
-//                   position order equals the page order for tie-breaking.
+//   merge_sorted_kernel : grid (Hkv, B).  With several chunks of at most
+//                   256 pages (and k2 <= 256), every block writes its chunk's
+//                   candidates in rank order, and the merge folds the sorted
+//                   lists pairwise (bitonic top-k2 of two lists per wave) and
+//                   sorts the winners by page.
+//   merge_kernel  : grid (Hkv, B).  Otherwise: a radix top-k2 over the
+//                   chunks' candidates, which are stored chunk-major in
+//                   ascending page order, so the position order equals the
+//                   page order for tie-breaking.
 #include <stdlib.h>
 
 #include <type_traits>
@@ -26,6 +32,14 @@ namespace {
 constexpr int kSelBlock = 256;
 constexpr int kMaxChunk = 2048;
 constexpr int kStageBytes = 48 * 1024;  // staged summaries
+// Sorted multi-chunk mode: a chunk holds at most one page per thread, so the
+// rank count gives every page's exact rank and the chunk's candidates are
+// written in rank order; the merge folds those sorted lists.  The select
+// block's LDS (about 45 KB) lets three blocks share a CU.
+constexpr int kSortedChunk = kSelBlock;
+constexpr int kSortedStageBytes = 32 * 1024;
+constexpr int kSortedMaxLists = 32;
+constexpr int kSortedMaxCand = 4096;
 
 struct SelArgs {
     int Hkv, P, max_pages, chunk, n_chunks, k1, k2;
@@ -41,8 +55,10 @@ struct SelArgs {
     int32_t *cand_page;
 };
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool SORTED>
 __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q, T *summ) {
+    constexpr int kChunkCap = SORTED ? kSortedChunk : kMaxChunk;
+    constexpr int kStageCap = SORTED ? kSortedStageBytes : kStageBytes;
     constexpr int NW = kSelBlock / kWave;
     __shared__ float qs[G][D];
     __shared__ float qsel[G][D];
@@ -50,8 +66,8 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
     constexpr bool kPacked = std::is_same<T, uint16_t>::value;
     __shared__ int ch_s[D];
     __shared__ T ovr_hi[D], ovr_lo[D];
-    __shared__ uint64_t comp_s[kMaxChunk];
-    constexpr int kStageElems = kStageBytes / (int)sizeof(T);
+    __shared__ uint64_t comp_s[kChunkCap];
+    constexpr int kStageElems = kStageCap / (int)sizeof(T);
     __shared__ __align__(16) T stage[kStageElems];
     __shared__ int cnt_s[kSelBlock];
     __shared__ uint32_t hist[256];
@@ -139,6 +155,18 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
         topk_ascending<kSelBlock>(comp_s, cnt, K, cnt_s, hist, sh, wave_tot,
                                   [&](int o, int i) { dst[o] = p0 + i; });
         for (int o = K + tid; o < k2; o += kSelBlock) dst[o] = -1;
+    } else if constexpr (SORTED) {
+        // cnt <= kSelBlock: exact ranks, candidates stored in rank order
+        // (score descending, then page ascending)
+        const int64_t base = (bh * a.n_chunks + ck) * k2;
+        rank_desc<kSelBlock>(comp_s, cnt, K, cnt_s, [&](int r, int i) {
+            a.cand_key[base + r] = (uint32_t)(comp_s[i] >> 32);
+            a.cand_page[base + r] = p0 + i;
+        });
+        for (int o = K + tid; o < k2; o += kSelBlock) {
+            a.cand_key[base + o] = 0u;  // below every finite score's key
+            a.cand_page[base + o] = -1;
+        }
     } else {
         const int64_t base = (bh * a.n_chunks + ck) * k2;
         topk_ascending<kSelBlock>(comp_s, cnt, K, cnt_s, hist, sh, wave_tot, [&](int o, int i) {
@@ -195,18 +223,143 @@ merge_kernel(int Hkv, int P, int max_pages, int n_chunks, const int32_t *seq_len
     for (int o = K + threadIdx.x; o < k2; o += kMergeBlock) dst[o] = -1;
 }
 
+// ---- merge of rank-ordered candidate lists --------------------------------
+// A list of L = E * 64 keys is held by one wave, key i = e * 64 + lane in
+// v[e].  cx_stage is one compare-exchange stage at distance J: of each pair
+// (i, i + J) the lower index keeps the larger key when up(i) holds, else the
+// smaller one.
+template <int E, int J, typename K, typename Up>
+__device__ __forceinline__ void cx_stage(K (&v)[E], int lane, Up up) {
+    if constexpr (J >= kWave) {
+        constexpr int R = J / kWave;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if ((e & R) == 0) {
+                const K a = v[e], b = v[e + R];
+                const bool hi_first = up(e * kWave + lane);
+                const K big = a > b ? a : b, small = a > b ? b : a;
+                v[e] = hi_first ? big : small;
+                v[e + R] = hi_first ? small : big;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = bitonic_stage<J>(v[e], up(e * kWave + lane));
+    }
+}
+
+// Half-cleaner cascade: sorts a bitonic list of L keys descending.
+template <int E, int J, typename K>
+__device__ __forceinline__ void list_clean(K (&v)[E], int lane) {
+    cx_stage<E, J>(v, lane, [](int i) { return (i & J) == 0; });
+    if constexpr (J > 1) list_clean<E, J / 2>(v, lane);
+}
+
+template <int E, int M, int J, typename K>
+__device__ __forceinline__ void list_merge(K (&v)[E], int lane) {
+    cx_stage<E, J>(v, lane, [](int i) { return ((i & M) == 0) == ((i & J) == 0); });
+    if constexpr (J > 1) list_merge<E, M, J / 2>(v, lane);
+}
+
+// Full bitonic sort of L keys, descending.
+template <int E, int M, typename K>
+__device__ __forceinline__ void list_sort(K (&v)[E], int lane) {
+    list_merge<E, M, M / 2>(v, lane);
+    if constexpr (M < E * kWave) list_sort<E, M * 2>(v, lane);
+}
+
+// Top-k2 over the chunks' rank-ordered candidates of one (sequence, KV
+// head): one block of 1,024 threads.  As 64-bit keys (score key, then the
+// complemented page) every list is descending and every real key is unique
+// and nonzero (padding is 0).  Waves fold pairs of lists in rounds: the
+// element-wise maximum of a descending list and a reversed one is bitonic and
+// holds the L largest keys of both, which a half-cleaner cascade sorts.  The
+// last list holds the top L; wave 0 sorts its first K by page and writes
+// them in ascending order.
+template <int E>
+__global__ void __launch_bounds__(kMergeBlock)
+merge_sorted_kernel(int Hkv, int P, int max_pages, int n_chunks, const int32_t *seq_lens, int k2,
+                    const uint32_t *cand_key, const int32_t *cand_page, int32_t *page_out) {
+    constexpr int L = E * kWave;
+    __shared__ uint64_t buf[2][kSortedMaxCand];
+    const int b = blockIdx.y, h = blockIdx.x, tid = threadIdx.x;
+    const int w = tid / kWave, lane = tid & (kWave - 1);
+    const int64_t bh = (int64_t)b * Hkv + h;
+    const int64_t cap = (int64_t)max_pages * P;
+    const int64_t n = min<int64_t>(max<int64_t>(seq_lens[b], 0), cap);
+    const int NP = (int)((n + P - 1) / P);
+    const int K = min(k2, NP);
+    const int m = n_chunks * k2;
+    const uint32_t *keys = cand_key + bh * m;
+    const int32_t *pages = cand_page + bh * m;
+    int32_t *dst = page_out + bh * k2;
+    for (int i = tid; i < n_chunks * L; i += kMergeBlock) {
+        const int l = i / L, r = i - l * L;
+        uint64_t ck = 0ull;
+        if (r < k2) {
+            const int j = l * k2 + r;
+            ck = ((uint64_t)keys[j] << 32) | (uint64_t)(~(uint32_t)pages[j]);
+        }
+        buf[0][i] = ck;
+    }
+    int src = 0, nl = n_chunks;
+    while (nl > 1) {
+        lds_barrier();
+        const int half = (nl + 1) / 2;
+        if (w < half) {
+            uint64_t v[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = buf[src][(2 * w) * L + e * kWave + lane];
+            if (2 * w + 1 < nl) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const uint64_t o = buf[src][(2 * w + 1) * L + (L - 1) - (e * kWave + lane)];
+                    v[e] = o > v[e] ? o : v[e];
+                }
+                list_clean<E, L / 2>(v, lane);
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) buf[1 - src][w * L + e * kWave + lane] = v[e];
+        }
+        src = 1 - src;
+        nl = half;
+    }
+    lds_barrier();
+    if (w == 0) {
+        // ~page of the K winners, sorted descending = page ascending; the
+        // other slots carry 0 and sort last
+        uint32_t inv[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = e * kWave + lane;
+            inv[e] = i < K ? (uint32_t)buf[src][i] : 0u;
+        }
+        list_sort<E, 2>(inv, lane);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = e * kWave + lane;
+            if (i < K) dst[i] = (int)~inv[e];
+        }
+    }
+    for (int o = K + tid; o < k2; o += kMergeBlock) dst[o] = -1;
+}
+
 template <typename T, int D, int G>
-void launch_t(dim3 grid, hipStream_t s, const SelArgs &a, const void *q, void *summ) {
-    select_kernel<T, D, G><<<grid, kSelBlock, 0, s>>>(a, (const T *)q, (T *)summ);
+void launch_t(dim3 grid, bool sorted, hipStream_t s, const SelArgs &a, const void *q, void *summ) {
+    if (sorted)
+        select_kernel<T, D, G, true><<<grid, kSelBlock, 0, s>>>(a, (const T *)q, (T *)summ);
+    else
+        select_kernel<T, D, G, false><<<grid, kSelBlock, 0, s>>>(a, (const T *)q, (T *)summ);
 }
 
 template <typename T, int D>
-bool dispatch_g(int G, dim3 grid, hipStream_t s, const SelArgs &a, const void *q, void *summ) {
+bool dispatch_g(int G, dim3 grid, bool sorted, hipStream_t s, const SelArgs &a, const void *q,
+                void *summ) {
     switch (G) {
-        case 1: launch_t<T, D, 1>(grid, s, a, q, summ); return true;
-        case 2: launch_t<T, D, 2>(grid, s, a, q, summ); return true;
-        case 4: launch_t<T, D, 4>(grid, s, a, q, summ); return true;
-        case 8: launch_t<T, D, 8>(grid, s, a, q, summ); return true;
+        case 1: launch_t<T, D, 1>(grid, sorted, s, a, q, summ); return true;
+        case 2: launch_t<T, D, 2>(grid, sorted, s, a, q, summ); return true;
+        case 4: launch_t<T, D, 4>(grid, sorted, s, a, q, summ); return true;
+        case 8: launch_t<T, D, 8>(grid, sorted, s, a, q, summ); return true;
     }
     return false;
 }
@@ -219,7 +372,6 @@ int env_int(const char *name, int dflt) {
 }  // namespace
 
 SelectPlan plan_select(const rkv_gqa &g, int B, int max_pages, int k2) {
-    (void)k2;
     const int units = B * g.n_kv_heads;
     int chunk = env_int("RKV_SELECT_CHUNK", 0);
     if (chunk <= 0) {
@@ -238,6 +390,18 @@ SelectPlan plan_select(const rkv_gqa &g, int B, int max_pages, int k2) {
     p.chunk_pages = chunk;
     p.n_chunks = (max_pages + chunk - 1) / chunk;
     if (p.n_chunks < 1) p.n_chunks = 1;
+    p.sorted = 0;
+    if (p.n_chunks > 1 && k2 <= 4 * kWave && env_int("RKV_SELECT_SORTED", 1) != 0) {
+        // elements per lane of a merge list: k2 rounded up to 64, 128 or 256
+        const int E = k2 <= kWave ? 1 : (k2 <= 2 * kWave ? 2 : 4);
+        const int sc = chunk < kSortedChunk ? chunk : kSortedChunk;
+        const int nch = (max_pages + sc - 1) / sc;
+        if (nch > 1 && nch <= kSortedMaxLists && nch * E * kWave <= kSortedMaxCand) {
+            p.chunk_pages = sc;
+            p.n_chunks = nch;
+            p.sorted = E;
+        }
+    }
     return p;
 }
 
@@ -283,17 +447,28 @@ int launch_select(const rkv_gqa &g, int dtype, int B, const void *q, const int32
     bool ok = false;
     const int d = g.head_dim;
     if (dtype == RKV_F32) {
-        if (d == 64) ok = dispatch_g<float, 64>(g.group, grid, s, a, q, summaries);
-        else if (d == 128) ok = dispatch_g<float, 128>(g.group, grid, s, a, q, summaries);
+        if (d == 64) ok = dispatch_g<float, 64>(g.group, grid, pl.sorted, s, a, q, summaries);
+        else if (d == 128) ok = dispatch_g<float, 128>(g.group, grid, pl.sorted, s, a, q, summaries);
     } else {
-        if (d == 64) ok = dispatch_g<uint16_t, 64>(g.group, grid, s, a, q, summaries);
-        else if (d == 128) ok = dispatch_g<uint16_t, 128>(g.group, grid, s, a, q, summaries);
+        if (d == 64) ok = dispatch_g<uint16_t, 64>(g.group, grid, pl.sorted, s, a, q, summaries);
+        else if (d == 128) ok = dispatch_g<uint16_t, 128>(g.group, grid, pl.sorted, s, a, q, summaries);
     }
     if (!ok) return RKV_EUNSUPPORTED;
     int st = launch_status();
     if (st != RKV_OK || pl.n_chunks == 1) return st;
-    merge_kernel<<<dim3(g.n_kv_heads, B), kMergeBlock, 0, s>>>(
-        g.n_kv_heads, P, max_pages, pl.n_chunks, seq_lens, k2, a.cand_key, a.cand_page, page_idx);
+    const dim3 mgrid(g.n_kv_heads, B);
+    if (pl.sorted == 1)
+        merge_sorted_kernel<1><<<mgrid, kMergeBlock, 0, s>>>(
+            g.n_kv_heads, P, max_pages, pl.n_chunks, seq_lens, k2, a.cand_key, a.cand_page, page_idx);
+    else if (pl.sorted == 2)
+        merge_sorted_kernel<2><<<mgrid, kMergeBlock, 0, s>>>(
+            g.n_kv_heads, P, max_pages, pl.n_chunks, seq_lens, k2, a.cand_key, a.cand_page, page_idx);
+    else if (pl.sorted == 4)
+        merge_sorted_kernel<4><<<mgrid, kMergeBlock, 0, s>>>(
+            g.n_kv_heads, P, max_pages, pl.n_chunks, seq_lens, k2, a.cand_key, a.cand_page, page_idx);
+    else
+        merge_kernel<<<dim3(g.n_kv_heads, B), kMergeBlock, 0, s>>>(
+            g.n_kv_heads, P, max_pages, pl.n_chunks, seq_lens, k2, a.cand_key, a.cand_page, page_idx);
     return launch_status();
 }
 

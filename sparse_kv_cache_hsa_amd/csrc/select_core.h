@@ -117,15 +117,13 @@ __device__ void topk_small(uint64_t key, int n, int K, uint64_t *sorted_s, Emit 
     }
 }
 
-// Rank count for n <= BLOCK composite keys comp_s[0..n) (LDS): every key is
-// compared with every other, the comparisons of one key spread over
-// BLOCK/n threads; then emit(pos, i) for the K largest, i ascending.
-// cnt_s is LDS scratch of n ints.  All threads must call it; comp_s must be
-// visible to the block.
-template <int BLOCK, typename Emit>
-__device__ void rank_topk(const uint64_t *comp_s, int n, int K, int *cnt_s, int *wave_tot,
-                          Emit emit) {
-    constexpr int NW = BLOCK / kWave;
+// Rank count for n <= BLOCK composite keys comp_s[0..n) (LDS): cnt_s[i] =
+// the number of keys larger than key i.  Every key is compared with every
+// other, the comparisons of one key spread over BLOCK/n threads.  cnt_s is
+// LDS scratch of n ints.  All threads must call it; comp_s must be visible
+// to the block; cnt_s is visible to the block on return.
+template <int BLOCK>
+__device__ void rank_count(const uint64_t *comp_s, int n, int *cnt_s) {
     const int tid = threadIdx.x;
     const int npad = (n + kWave - 1) / kWave * kWave;
     int parts = npad > 0 ? BLOCK / npad : 1;
@@ -146,10 +144,29 @@ __device__ void rank_topk(const uint64_t *comp_s, int n, int K, int *cnt_s, int 
         else cnt_s[i] = c;
     }
     lds_barrier();
+}
+
+// Top-K by rank count: emit(pos, i) for the K largest of comp_s[0..n),
+// i ascending.  Same contract as rank_count.
+template <int BLOCK, typename Emit>
+__device__ void rank_topk(const uint64_t *comp_s, int n, int K, int *cnt_s, int *wave_tot,
+                          Emit emit) {
+    constexpr int NW = BLOCK / kWave;
+    const int tid = threadIdx.x;
+    rank_count<BLOCK>(comp_s, n, cnt_s);
     const bool sel = tid < n && cnt_s[tid] < K;
     int tot;
     const int pos = block_excl_count<NW>(sel, wave_tot, tot);
     if (sel) emit(pos, tid);
+}
+
+// Top-K by rank count in rank order: emit(r, i) for the key i of rank r < K
+// (rank 0 is the largest).  Same contract as rank_count.
+template <int BLOCK, typename Emit>
+__device__ void rank_desc(const uint64_t *comp_s, int n, int K, int *cnt_s, Emit emit) {
+    rank_count<BLOCK>(comp_s, n, cnt_s);
+    const int tid = threadIdx.x;
+    if (tid < n && cnt_s[tid] < K) emit(cnt_s[tid], tid);
 }
 
 // Channel ranking.  qs must be visible to the block.  On return ch_s[0..k1)

@@ -109,14 +109,18 @@ def run_decode_case(case, seed, q_override=None, k_override=None, mode="decode")
     return worst, out
 
 
-@pytest.fixture(params=["auto", "fused", "splitk", "split"])
+@pytest.fixture(params=["auto", "fused", "splitk", "split", "split-legacy"])
 def path(request, monkeypatch):
     """Which implementation rkv_hsa_decode / rkv_decode_step dispatch to:
     the default rule, the fused kernel with one block per unit, the fused
-    kernel split K-wise (plus the merge), or the standalone kernels."""
-    env = {"fused": "1", "splitk": "2", "split": "0"}.get(request.param)
+    kernel split K-wise (plus the merge), or the standalone kernels (with
+    several selection chunks: rank-ordered candidates and the rank-search
+    merge by default, "split-legacy" the radix top-k and radix merge)."""
+    env = {"fused": "1", "splitk": "2", "split": "0", "split-legacy": "0"}.get(request.param)
     if env is not None:
         monkeypatch.setenv("RKV_FUSED", env)
+    if request.param == "split-legacy":
+        monkeypatch.setenv("RKV_SELECT_SORTED", "0")
     return request.param
 
 
