@@ -76,7 +76,9 @@ def build(verbose: bool = False) -> str:
             if verbose and warn:
                 print(warn)
     tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    # --no-undefined: a kernel whose host-side launch stub was not emitted
+    # fails here instead of at load time
+    cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,--no-undefined", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
