@@ -203,7 +203,10 @@ logits_tiled_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, const T 
         }
         float *zr = Z + (bh * L_max + t0 + tt) * R + r0 + rt * 4;
         if (r0 + rt * 4 + 3 < R && ((R & 3) == 0)) {
-            *(float4 *)zr = make_float4(z[0], z[1], z[2], z[3]);
+            // the logits are streamed: written once here, read once by each
+            // of the two later passes (non-temporal hint on all three)
+            typedef float f32x4 __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(f32x4{z[0], z[1], z[2], z[3]}, (f32x4 *)zr);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -297,7 +300,7 @@ rowsum_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, int nch, const
                 float z[kBatch];
 #pragma unroll
                 for (int u = 0; u < kBatch; ++u)
-                    z[u] = tb + u < a1 ? Z[(bh * L_max + tb + u) * R + r] : 0.0f;
+                    z[u] = tb + u < a1 ? __builtin_nontemporal_load(&Z[(bh * L_max + tb + u) * R + r]) : 0.0f;
 #pragma unroll
                 for (int u = 0; u < kBatch; ++u)
                     if (tb + u < a1) acc += (double)expf(z[u] - mr);
@@ -401,7 +404,7 @@ colsum_tiled_kernel(int Hkv, int G, int w, int64_t L_max, EvictSeq seq, const fl
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int tt = tb + u * per;
-                z[u] = tt < nk ? Z[(bh * L_max + t0 + tt) * R + r] : 0.0f;
+                z[u] = tt < nk ? __builtin_nontemporal_load(&Z[(bh * L_max + t0 + tt) * R + r]) : 0.0f;
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {

@@ -39,6 +39,9 @@ DECODE_CASES = [
     (BF16, 2, 2, 4, 128, 256, 1, 1, [3000, 256], 16),
     (BF16, 3, 2, 2, 64, 16, 1, 1, [1, 16, 17], 4),
     (BF16, 2, 2, 4, 128, 16, 32, 64, [2048, 2047], 128),
+    # k2 in (128, 256] over several selection chunks: the rank-ordered
+    # candidate merge with four keys per lane
+    (BF16, 1, 2, 4, 128, 8, 32, 200, [4000], 600),
 ]
 
 
