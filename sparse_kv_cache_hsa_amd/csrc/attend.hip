@@ -84,7 +84,9 @@ attend_kernel(AttArgs a, const T *k_pool, const T *v_pool, const T *q) {
 // block (h, b, j), one thread per channel.  M = max of the splits' m and
 // Ls = sum of l_s 2^(m_s - M) come from wave reductions in a fixed order; the
 // split weights 2^(m_s - M) go to LDS, and each channel then sums its split
-// partials in split order with batches of loads in flight.
+// partials in split order.  The partials of the first 16 splits and the
+// splits' (m, l) are loaded up front, so the usual case costs one memory
+// round trip.
 constexpr int kMergeMaxSplits = 1024;
 
 template <int D, int G>
@@ -98,8 +100,19 @@ attend_merge_kernel(int Hkv, int n_splits, const float *part, float *out) {
     const int64_t bh = (int64_t)b * Hkv + h;
     const int64_t stride = (int64_t)G * (D + 2);
     const float *base_p = part + (bh * n_splits * G + j) * (D + 2);
-    float m = -INFINITY;
-    for (int sp = c; sp < n_splits; sp += D) m = fmaxf(m, base_p[sp * stride + D]);
+    // One memory round trip for the common case: the channel's partials of
+    // the first kPre splits and (thread sp) split sp's max and sum are all
+    // loaded before any of them is used.
+    constexpr int kPre = 16;
+    float pre[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+        pre[u] = u < n_splits ? base_p[(int64_t)u * stride + c] : 0.0f;
+    const bool own = c < n_splits;
+    const float m_own = own ? base_p[(int64_t)c * stride + D] : -INFINITY;
+    const float l_own = own ? base_p[(int64_t)c * stride + D + 1] : 0.0f;
+    float m = m_own;
+    for (int sp = c + D; sp < n_splits; sp += D) m = fmaxf(m, base_p[sp * stride + D]);
     m = pair_max<1>(m);
     m = pair_max<2>(m);
     m = pair_max<4>(m);
@@ -112,7 +125,12 @@ attend_merge_kernel(int Hkv, int n_splits, const float *part, float *out) {
 #pragma unroll
     for (int i = 1; i < NW; ++i) M = fmaxf(M, red_s[0][i]);
     float ls = 0.0f;
-    for (int sp = c; sp < n_splits; sp += D) {
+    if (own) {
+        const float wt = exp2_diff(m_own, M);
+        cw_s[c] = wt;
+        ls = l_own * wt;
+    }
+    for (int sp = c + D; sp < n_splits; sp += D) {
         const float wt = exp2_diff(base_p[sp * stride + D], M);
         cw_s[sp] = wt;
         ls += base_p[sp * stride + D + 1] * wt;
@@ -128,9 +146,13 @@ attend_merge_kernel(int Hkv, int n_splits, const float *part, float *out) {
     float Ls = red_s[1][0];
 #pragma unroll
     for (int i = 1; i < NW; ++i) Ls += red_s[1][i];
-    constexpr int kBatch = 8;
+    // the channel's sum over the splits, in split order
     float A = 0.0f;
-    for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+        if (u < n_splits) A += pre[u] * cw_s[u];
+    constexpr int kBatch = 8;
+    for (int s0 = kPre; s0 < n_splits; s0 += kBatch) {
         float v[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
