@@ -12,8 +12,9 @@
 //                   K/V row, folds it into that page's summary and scores the
 //                   page from the new summary (no other block reads it).
 //   merge_sorted_kernel : grid (Hkv, B).  With several chunks of at most
-//                   256 pages (and k2 <= 256), every block writes its chunk's
-//                   candidates in rank order, and the merge folds the sorted
+//                   256 pages (and k2 <= 256), every block sorts its chunk's
+//                   keys and writes its candidates in rank order, and the
+//                   merge folds the sorted
 //                   lists pairwise (bitonic top-k2 of two lists per wave) and
 //                   sorts the winners by page.
 //   merge_kernel  : grid (Hkv, B).  Otherwise: a radix top-k2 over the
@@ -32,10 +33,10 @@ namespace {
 constexpr int kSelBlock = 256;
 constexpr int kMaxChunk = 2048;
 constexpr int kStageBytes = 48 * 1024;  // staged summaries
-// Sorted multi-chunk mode: a chunk holds at most one page per thread, so the
-// rank count gives every page's exact rank and the chunk's candidates are
-// written in rank order; the merge folds those sorted lists.  The select
-// block's LDS (about 45 KB) lets three blocks share a CU.
+// Sorted multi-chunk mode: a chunk holds at most one page per thread (256),
+// a sorting network over the block gives the chunk's candidates in rank
+// order, and the merge folds those sorted lists.  The select block's LDS
+// (about 45 KB) lets three blocks share a CU.
 constexpr int kSortedChunk = kSelBlock;
 constexpr int kSortedStageBytes = 32 * 1024;
 constexpr int kSortedMaxLists = 32;
@@ -54,6 +55,87 @@ struct SelArgs {
     uint32_t *cand_key;
     int32_t *cand_page;
 };
+
+// ---- bitonic lists held by one wave ----------------------------------------
+// A list of L = E * 64 keys is held by one wave, key i = e * 64 + lane in
+// v[e].  cx_stage is one compare-exchange stage at distance J: of each pair
+// (i, i + J) the lower index keeps the larger key when up(i) holds, else the
+// smaller one.
+template <int E, int J, typename K, typename Up>
+__device__ __forceinline__ void cx_stage(K (&v)[E], int lane, Up up) {
+    if constexpr (J >= kWave) {
+        constexpr int R = J / kWave;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if ((e & R) == 0) {
+                const K a = v[e], b = v[e + R];
+                const bool hi_first = up(e * kWave + lane);
+                const K big = a > b ? a : b, small = a > b ? b : a;
+                v[e] = hi_first ? big : small;
+                v[e + R] = hi_first ? small : big;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = bitonic_stage<J>(v[e], up(e * kWave + lane));
+    }
+}
+
+// Half-cleaner cascade: sorts a bitonic list of L keys descending.
+template <int E, int J, typename K>
+__device__ __forceinline__ void list_clean(K (&v)[E], int lane) {
+    cx_stage<E, J>(v, lane, [](int i) { return (i & J) == 0; });
+    if constexpr (J > 1) list_clean<E, J / 2>(v, lane);
+}
+
+template <int E, int M, int J, typename K>
+__device__ __forceinline__ void list_merge(K (&v)[E], int lane) {
+    cx_stage<E, J>(v, lane, [](int i) { return ((i & M) == 0) == ((i & J) == 0); });
+    if constexpr (J > 1) list_merge<E, M, J / 2>(v, lane);
+}
+
+// Full bitonic sort of L keys, descending.
+template <int E, int M, typename K>
+__device__ __forceinline__ void list_sort(K (&v)[E], int lane) {
+    list_merge<E, M, M / 2>(v, lane);
+    if constexpr (M < E * kWave) list_sort<E, M * 2>(v, lane);
+}
+
+// The K <= 256 largest of a chunk's 256 keys (key i held by thread i of
+// the 4-wave block, 0 for pages past the chunk) in descending order:
+// emit(r, key) for r < K.  Every wave sorts its 64 keys; waves 0 and 2 merge
+// their neighbour's list into a sorted 128 (own list, then the other list
+// reversed, is bitonic); wave 0 merges the two 128-lists the same way into
+// all 256 keys, sorted.  buf: LDS of 256 keys.  All threads must call it;
+// the caller synchronises the block before reusing buf.
+template <typename Emit>
+__device__ __forceinline__ void chunk_sorted_topk(uint64_t key, int K, uint64_t *buf, Emit emit) {
+    static_assert(kSelBlock == 4 * kWave, "four waves");
+    const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
+    key = wave_sort_desc(key);
+    buf[tid] = key;
+    lds_barrier();
+    if (w == 0 || w == 2) {
+        uint64_t v[2];
+        v[0] = key;
+        v[1] = buf[(w + 1) * kWave + (kWave - 1 - lane)];
+        list_clean<2, kWave>(v, lane);
+        buf[w * kWave + lane] = v[0];
+        buf[w * kWave + kWave + lane] = v[1];
+    }
+    lds_barrier();
+    if (w == 0) {
+        uint64_t v[4];
+        v[0] = buf[lane];
+        v[1] = buf[kWave + lane];
+        v[2] = buf[4 * kWave - 1 - lane];
+        v[3] = buf[3 * kWave - 1 - lane];
+        list_clean<4, 2 * kWave>(v, lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e * kWave + lane < K) emit(e * kWave + lane, v[e]);
+    }
+}
 
 template <typename T, int D, int G, bool SORTED>
 __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q, T *summ) {
@@ -159,9 +241,11 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
         // cnt <= kSelBlock: exact ranks, candidates stored in rank order
         // (score descending, then page ascending)
         const int64_t base = (bh * a.n_chunks + ck) * k2;
-        rank_desc<kSelBlock>(comp_s, cnt, K, cnt_s, [&](int r, int i) {
-            a.cand_key[base + r] = (uint32_t)(comp_s[i] >> 32);
-            a.cand_page[base + r] = p0 + i;
+        const uint64_t key = tid < cnt ? comp_s[tid] : 0ull;
+        lds_barrier();  // comp_s is reused as the merge buffer
+        chunk_sorted_topk(key, K, comp_s, [&](int r, uint64_t kk) {
+            a.cand_key[base + r] = (uint32_t)(kk >> 32);
+            a.cand_page[base + r] = p0 + (int)~(uint32_t)kk;
         });
         for (int o = K + tid; o < k2; o += kSelBlock) {
             a.cand_key[base + o] = 0u;  // below every finite score's key
@@ -221,51 +305,6 @@ merge_kernel(int Hkv, int P, int max_pages, int n_chunks, const int32_t *seq_len
         }
     }
     for (int o = K + threadIdx.x; o < k2; o += kMergeBlock) dst[o] = -1;
-}
-
-// ---- merge of rank-ordered candidate lists --------------------------------
-// A list of L = E * 64 keys is held by one wave, key i = e * 64 + lane in
-// v[e].  cx_stage is one compare-exchange stage at distance J: of each pair
-// (i, i + J) the lower index keeps the larger key when up(i) holds, else the
-// smaller one.
-template <int E, int J, typename K, typename Up>
-__device__ __forceinline__ void cx_stage(K (&v)[E], int lane, Up up) {
-    if constexpr (J >= kWave) {
-        constexpr int R = J / kWave;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if ((e & R) == 0) {
-                const K a = v[e], b = v[e + R];
-                const bool hi_first = up(e * kWave + lane);
-                const K big = a > b ? a : b, small = a > b ? b : a;
-                v[e] = hi_first ? big : small;
-                v[e + R] = hi_first ? small : big;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = bitonic_stage<J>(v[e], up(e * kWave + lane));
-    }
-}
-
-// Half-cleaner cascade: sorts a bitonic list of L keys descending.
-template <int E, int J, typename K>
-__device__ __forceinline__ void list_clean(K (&v)[E], int lane) {
-    cx_stage<E, J>(v, lane, [](int i) { return (i & J) == 0; });
-    if constexpr (J > 1) list_clean<E, J / 2>(v, lane);
-}
-
-template <int E, int M, int J, typename K>
-__device__ __forceinline__ void list_merge(K (&v)[E], int lane) {
-    cx_stage<E, J>(v, lane, [](int i) { return ((i & M) == 0) == ((i & J) == 0); });
-    if constexpr (J > 1) list_merge<E, M, J / 2>(v, lane);
-}
-
-// Full bitonic sort of L keys, descending.
-template <int E, int M, typename K>
-__device__ __forceinline__ void list_sort(K (&v)[E], int lane) {
-    list_merge<E, M, M / 2>(v, lane);
-    if constexpr (M < E * kWave) list_sort<E, M * 2>(v, lane);
 }
 
 // Top-k2 over the chunks' rank-ordered candidates of one (sequence, KV

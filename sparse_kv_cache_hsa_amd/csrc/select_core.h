@@ -160,15 +160,6 @@ __device__ void rank_topk(const uint64_t *comp_s, int n, int K, int *cnt_s, int 
     if (sel) emit(pos, tid);
 }
 
-// Top-K by rank count in rank order: emit(r, i) for the key i of rank r < K
-// (rank 0 is the largest).  Same contract as rank_count.
-template <int BLOCK, typename Emit>
-__device__ void rank_desc(const uint64_t *comp_s, int n, int K, int *cnt_s, Emit emit) {
-    rank_count<BLOCK>(comp_s, n, cnt_s);
-    const int tid = threadIdx.x;
-    if (tid < n && cnt_s[tid] < K) emit(cnt_s[tid], tid);
-}
-
 // Channel ranking.  qs must be visible to the block.  On return ch_s[0..k1)
 // holds the chosen channels in ascending order and qsel[j][i] = qs[j][ch_s[i]]
 // (both visible to the block); if qpm is given (bf16 queries), also the
