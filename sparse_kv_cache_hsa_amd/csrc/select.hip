@@ -13,10 +13,9 @@
 //                   page from the new summary (no other block reads it).
 //   merge_sorted_kernel : grid (Hkv, B).  With several chunks of at most
 //                   256 pages (and k2 <= 256), every block sorts its chunk's
-//                   keys and writes its candidates in rank order, and the
-//                   merge folds the sorted
-//                   lists pairwise (bitonic top-k2 of two lists per wave) and
-//                   sorts the winners by page.
+//                   keys and writes its candidates in rank order; the merge
+//                   folds the sorted lists pairwise (the bitonic top k2 of
+//                   two lists per wave) and sorts the winners by page.
 //   merge_kernel  : grid (Hkv, B).  Otherwise: a radix top-k2 over the
 //                   chunks' candidates, which are stored chunk-major in
 //                   ascending page order, so the position order equals the
