@@ -485,11 +485,11 @@ int launch_select(const rkv_gqa &g, int dtype, int B, const void *q, const int32
     bool ok = false;
     const int d = g.head_dim;
     if (dtype == RKV_F32) {
-        if (d == 64) ok = dispatch_g<float, 64>(g.group, grid, pl.sorted, s, a, q, summaries);
-        else if (d == 128) ok = dispatch_g<float, 128>(g.group, grid, pl.sorted, s, a, q, summaries);
+        if (d == 64) ok = dispatch_g<float, 64>(g.group, grid, pl.sorted != 0, s, a, q, summaries);
+        else if (d == 128) ok = dispatch_g<float, 128>(g.group, grid, pl.sorted != 0, s, a, q, summaries);
     } else {
-        if (d == 64) ok = dispatch_g<uint16_t, 64>(g.group, grid, pl.sorted, s, a, q, summaries);
-        else if (d == 128) ok = dispatch_g<uint16_t, 128>(g.group, grid, pl.sorted, s, a, q, summaries);
+        if (d == 64) ok = dispatch_g<uint16_t, 64>(g.group, grid, pl.sorted != 0, s, a, q, summaries);
+        else if (d == 128) ok = dispatch_g<uint16_t, 128>(g.group, grid, pl.sorted != 0, s, a, q, summaries);
     }
     if (!ok) return RKV_EUNSUPPORTED;
     int st = launch_status();
