@@ -197,7 +197,7 @@ int launch_t(const rkv_gqa &g, int B, const void *q, const rkv_paged_cache &c,
         case 1: attend_kernel<T, D, G, 8, 2, true><<<grid, 8 * kWave, 0, s>>>(a, kp, vp, qp); break;
         case 2: attend_kernel<T, D, G, 16, 4, false><<<grid, 16 * kWave, 0, s>>>(a, kp, vp, qp); break;
         case 3: attend_kernel<T, D, G, 16, 2, true><<<grid, 16 * kWave, 0, s>>>(a, kp, vp, qp); break;
-        default: attend_kernel<T, D, G, 4, 4, false><<<grid, 4 * kWave, 0, s>>>(a, kp, vp, qp); break;
+        default: attend_kernel<T, D, G, 4, 8, false><<<grid, 4 * kWave, 0, s>>>(a, kp, vp, qp); break;
     }
     int st = launch_status();
     if (st != RKV_OK || pl.n_splits == 1) return st;
