@@ -255,8 +255,9 @@ def main():
     per_layer, _, n_new = inputs[W + K - 1]
     mode = rkv.decode_mode(sess.g, sess.B, sess.P, sess.max_pages, wl.k2, wl.k1,
                            rkv.RKV_BF16 if wl.dtype.itemsize == 2 else rkv.RKV_F32)
-    if mode in (1, 2):
-        kernel = "decode_kernel" if mode == 1 else "decode_kernel split-K + attend_merge_kernel"
+    if mode in (rkv.RKV_FORM_FUSED, rkv.RKV_FORM_SPLITK):
+        kernel = ("decode_kernel" if mode == rkv.RKV_FORM_FUSED
+                  else "decode_kernel split-K + attend_merge_kernel")
         launch_us = ms_total * 1e3 / (K * sess.n_layers)
         bytes_launch = step_b / sess.n_layers
     else:
@@ -316,7 +317,8 @@ def main():
                    "prompt_len_min": min(sess.prompt_lens), "prompt_len_max": max(sess.prompt_lens),
                    "kept_rows_min": min(sess.keep), "kept_rows_max": max(sess.keep),
                    "graph": not args.no_graph,
-                   "path": {0: "standalone kernels", 1: "fused", 2: "fused split-K"}[mode],
+                   "path": {rkv.RKV_FORM_STANDALONE: "standalone kernels", rkv.RKV_FORM_FUSED: "fused",
+                            rkv.RKV_FORM_SPLITK: "fused split-K"}[mode],
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(kern_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),

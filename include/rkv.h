@@ -20,11 +20,17 @@
  *    different streams are independent as long as their buffers are.
  *  - Every call returns an rkv status (0 = RKV_OK).  Arguments are checked on
  *    the host before anything is enqueued; a failed check enqueues nothing.
- *    Values that live in device memory (sequence lengths, page tables) cannot
- *    be checked on the host: kernels clamp them so that no access leaves the
- *    buffers described here (a length is clamped to the cache capacity, a
- *    page whose physical block is outside [0, num_blocks) is treated as
- *    empty); results for such inputs are defined but meaningless.
+ *    Lengths known on the host that do not fit the cache give RKV_ECAPACITY.
+ *    Values that live in device memory (sequence lengths, page tables, page
+ *    lists) cannot be checked on the host: kernels keep every access inside
+ *    the buffers described here (a length is clamped to the cache capacity,
+ *    a page whose physical block is outside [0, num_blocks) contributes no
+ *    rows) and report each such input in the optional device status word of
+ *    rkv_opts (RKV_DEV_* flags below), so a caller that overruns the cache
+ *    can find out; results for such inputs are defined but meaningless.
+ *  - A HIP error left pending on the calling host thread by earlier runtime
+ *    calls is cleared when an entry point starts, so RKV_EHIP reports only
+ *    the launches of that call.
  *  - Element type `dtype` (RKV_F32 or RKV_BF16) applies to queries, keys,
  *    values and page summaries alike.  Attention outputs are always fp32.
  *  - GQA: query head h*G + j (j < G) reads KV head h.
@@ -88,6 +94,41 @@ typedef struct rkv_paged_cache {
  * selected channel is one contiguous run over the pages.  Among equal values
  * the earliest row's bits are kept, so an incremental append gives the same
  * bits as a rebuild ([P3] "Evidence"). */
+
+/* ---- execution options ---------------------------------------------------
+ * The last argument of every call that enqueues device work.  NULL, or a
+ * zero-initialised struct, means: the library picks every kernel form and
+ * size by its documented rule, and no status word is written.  The fields
+ * other than `status` fix how the decode calls run (tests and tuning); they
+ * never change results beyond the documented tolerances, and
+ * rkv_hsa_workspace_bytes must be given the same options as the calls whose
+ * workspace it sizes. */
+#define RKV_FORM_AUTO 0       /* the rule given at rkv_decode_step */
+#define RKV_FORM_STANDALONE 1 /* separate select and attention kernels */
+#define RKV_FORM_FUSED 2      /* one fused kernel, one block per (sequence, KV head) */
+#define RKV_FORM_SPLITK 3     /* the fused kernel split K-wise, plus a merge kernel */
+
+/* Device status flags, ORed into *rkv_opts.status by the kernels. */
+#define RKV_DEV_LENGTH 1 /* a row count was negative or beyond max_pages * P: clamped */
+#define RKV_DEV_BLOCK 2  /* a page-table entry in use was outside [0, num_blocks): skipped */
+#define RKV_DEV_PAGE 4   /* a page index given to rkv_hsa_attend was outside [0, NP): skipped */
+
+typedef struct rkv_opts {
+    int32_t form;           /* RKV_FORM_*; a form the shapes do not allow falls back to
+                               RKV_FORM_STANDALONE */
+    int32_t splitk_blocks;  /* RKV_FORM_SPLITK: blocks to aim for in all (0 = 128) */
+    int32_t select_chunk;   /* standalone selection: pages per block (0 = automatic) */
+    int32_t select_radix;   /* standalone selection over several chunks: 1 = radix top-k
+                               and radix merge instead of rank-ordered lists (0 = auto) */
+    int32_t attend_variant; /* standalone attention block shape, 1..4 (0 = automatic):
+                               1 = 4 waves, 8 rows of K and V per lane in flight;
+                               2 = 8 waves, pipelined; 3 = 16 waves; 4 = 16 waves,
+                               pipelined */
+    int32_t attend_pages;   /* standalone attention: selected pages per block
+                               (0 = automatic) */
+    int32_t *status;        /* device int32, optional: RKV_DEV_* flags are ORed in; the
+                               library never clears it */
+} rkv_opts;
 
 /* Human-readable text for a status code (static storage). */
 const char *rkv_status_string(int status);
@@ -157,7 +198,8 @@ int rkv_prefill_evict(const rkv_gqa *g, int32_t dtype, int32_t B,
                       const void *k, const void *v, const rkv_paged_cache *cache,
                       void *summaries, int32_t *kept_idx, int32_t keep_stride,
                       float *pooled_scores, int32_t *seq_lens_out, void *ws,
-                      size_t ws_bytes, void *stream);
+                      size_t ws_bytes, void *stream,
+                   const rkv_opts *opts);
 
 /* ---- chunked-prefill eviction -------------------------------------------- */
 /* [P3] "Evidence": stage-1 eviction re-enforces its budget across the calls
@@ -195,7 +237,8 @@ int rkv_prefill_evict_chunk(const rkv_gqa *g, int32_t dtype, int32_t B,
                             const void *k_chunk, const void *v_chunk,
                             const rkv_paged_cache *cache, void *summaries, int32_t *kept_idx,
                             int32_t keep_stride, float *pooled_scores, int32_t *seq_lens_out,
-                            void *ws, size_t ws_bytes, void *stream);
+                            void *ws, size_t ws_bytes, void *stream,
+                   const rkv_opts *opts);
 
 /* ---- incremental page-summary append ------------------------------------ */
 /* [P3] "Where it sits" (paged max/min) and "Evidence" (incremental update
@@ -213,7 +256,8 @@ int rkv_prefill_evict_chunk(const rkv_gqa *g, int32_t dtype, int32_t B,
 int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,
                          const rkv_paged_cache *cache, const int32_t *n_old,
                          const int32_t *n_new, int32_t max_new_rows, const void *k_src,
-                         const void *v_src, void *summaries, void *stream);
+                         const void *v_src, void *summaries, void *stream,
+                   const rkv_opts *opts);
 
 /* ---- Hybrid Sparse Attention decode ------------------------------------- */
 /* [P3] "Where it sits": scores are approximated by a two-dimensional
@@ -234,7 +278,9 @@ int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,
  * Arguments
  *   q            : device [B][Hq][d] decode queries, 16-byte aligned.
  *   seq_lens     : device [B] int32 rows per sequence (current token
- *                  included); clamped to [0, max_pages * P].
+ *                  included); clamped to [0, max_pages * P] (RKV_DEV_LENGTH).
+ *   page_idx, for rkv_hsa_attend: its first min(k2, NP) entries must be
+ *                  pages in [0, NP); others are skipped (RKV_DEV_PAGE).
  *   summaries    : device [B][Hkv][2][d][max_pages], current for seq_lens.
  *   k1, k2       : channels and pages kept.
  *   chan_idx     : device [B][Hkv][k1] int32, optional.
@@ -245,28 +291,33 @@ int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,
  *   scale        : logit scale (normally 1/sqrt(d)), finite and > 0.
  *   out          : device [B][Hq][d] fp32.
  *   ws, ws_bytes : device workspace of at least rkv_hsa_workspace_bytes(...)
- *                  for the same shapes; calls sharing one workspace must be
- *                  ordered on one stream.
+ *                  for the same shapes and options; calls sharing one
+ *                  workspace must be ordered on one stream.
+ *   opts         : execution options (NULL = automatic); see rkv_opts.
  * rkv_hsa_decode gives the results of rkv_hsa_select followed by
  * rkv_hsa_attend on `stream`; it runs as rkv_decode_step without an append
  * (one of the fused forms where the shapes allow).
  * Errors: RKV_EINVAL, RKV_EUNSUPPORTED, RKV_EWORKSPACE, RKV_EHIP. */
 size_t rkv_hsa_workspace_bytes(const rkv_gqa *g, int32_t B, int32_t page_size,
-                               int32_t max_pages, int32_t k1, int32_t k2);
+                               int32_t max_pages, int32_t k1, int32_t k2,
+                               const rkv_opts *opts);
 int rkv_hsa_select(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                    const int32_t *seq_lens, int32_t page_size, int32_t max_pages,
                    const void *summaries, int32_t k1, int32_t k2, int32_t *chan_idx,
                    int32_t *page_idx, float *page_scores, void *ws, size_t ws_bytes,
-                   void *stream);
+                   void *stream,
+                   const rkv_opts *opts);
 int rkv_hsa_attend(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                    const rkv_paged_cache *cache, const int32_t *seq_lens,
                    const int32_t *page_idx, int32_t k2, float scale, float *out, void *ws,
-                   size_t ws_bytes, void *stream);
+                   size_t ws_bytes, void *stream,
+                   const rkv_opts *opts);
 int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                    const rkv_paged_cache *cache, const int32_t *seq_lens,
                    const void *summaries, int32_t k1, int32_t k2, float scale, float *out,
                    int32_t *chan_idx, int32_t *page_idx, float *page_scores, void *ws,
-                   size_t ws_bytes, void *stream);
+                   size_t ws_bytes, void *stream,
+                   const rkv_opts *opts);
 
 /* ---- one decode step of one layer ---------------------------------------- */
 /* The per-layer hot path: append the new token, then HSA decode.  With
@@ -289,22 +340,23 @@ int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
  *     K-wise, about 128 blocks in all, each making the unit's selection and
  *     attending to a share of its pages, then a merge kernel (two launches);
  *   - otherwise the standalone append, select and attention kernels.
- * The environment variable RKV_FUSED=0/1/2 forces the standalone kernels,
- * the one-block fused kernel or the split-K form where the shapes allow.
+ * rkv_opts.form picks a form explicitly: RKV_FORM_FUSED wherever the fused
+ * limits hold, RKV_FORM_SPLITK where the stage also fits, else the
+ * standalone kernels.
  * Other arguments and errors as for rkv_hsa_decode. */
-/* Which form rkv_decode_step (and rkv_hsa_decode) takes for these shapes,
- * by the rule above and the current RKV_FUSED setting: 0 = the standalone
- * kernels, 1 = the fused kernel with one block per (sequence, KV head),
- * 2 = the fused kernel split K-wise plus the merge.  Host only, no device
- * work.  Errors: RKV_EINVAL (bad layout or sizes), RKV_EUNSUPPORTED (dtype). */
+/* Which form rkv_decode_step (and rkv_hsa_decode) takes for these shapes and
+ * options, by the rule above: RKV_FORM_STANDALONE, RKV_FORM_FUSED or
+ * RKV_FORM_SPLITK (never RKV_FORM_AUTO).  Host only, no device work.
+ * Errors: RKV_EINVAL (bad layout or sizes), RKV_EUNSUPPORTED (dtype). */
 int rkv_decode_mode(const rkv_gqa *g, int32_t dtype, int32_t B, int32_t page_size,
-                    int32_t max_pages, int32_t k1, int32_t k2);
+                    int32_t max_pages, int32_t k1, int32_t k2, const rkv_opts *opts);
 
 int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                     const void *k_new, const void *v_new, const rkv_paged_cache *cache,
                     const int32_t *seq_lens, void *summaries, int32_t k1, int32_t k2,
                     float scale, float *out, int32_t *chan_idx, int32_t *page_idx,
-                    float *page_scores, void *ws, size_t ws_bytes, void *stream);
+                    float *page_scores, void *ws, size_t ws_bytes, void *stream,
+                   const rkv_opts *opts);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -11,8 +11,6 @@
 // combines the splits in split order.  (Merging inside the kernel through an
 // arrival counter needs a device-scope release per block, which on this chip
 // writes back the whole L2 and costs far more than the extra launch.)
-#include <stdlib.h>
-
 #include "attend_core.h"
 
 namespace rkv {
@@ -26,6 +24,7 @@ struct AttArgs {
     const int32_t *page_table, *seq_lens, *page_idx;
     float qscale;
     float *out, *part;
+    int32_t *status;
 };
 
 template <typename T, int D, int G, int NW, int U, bool PIPE>
@@ -40,7 +39,7 @@ attend_kernel(AttArgs a, const T *k_pool, const T *v_pool, const T *q) {
     const int P = a.P;
     const int64_t bh = (int64_t)b * a.Hkv + h;
     const int64_t cap = (int64_t)a.max_pages * P;
-    const int64_t n = min<int64_t>(max<int64_t>(a.seq_lens[b], 0), cap);
+    const int64_t n = clamp_rows(a.seq_lens[b], cap, (sp == 0 && h == 0 && tid == 0) ? a.status : nullptr);
     const int NP = (int)((n + P - 1) / P);
     const int nsel = min(a.k2, NP);
     const int i0 = sp * a.ppb;
@@ -51,9 +50,16 @@ attend_kernel(AttArgs a, const T *k_pool, const T *v_pool, const T *q) {
         const int pi = f / P, slot = f - pi * P;
         const int32_t pg = a.page_idx[bh * a.k2 + i0 + pi];
         uint32_t r = kBadRow;
-        if (pg >= 0 && pg < NP && (int64_t)pg * P + slot < n) {
-            const int32_t blk = a.page_table[(int64_t)b * a.max_pages + pg];
-            if (blk >= 0 && blk < a.num_blocks) r = (uint32_t)(((int64_t)blk * a.Hkv + h) * P + slot);
+        if (pg >= 0 && pg < NP) {
+            if ((int64_t)pg * P + slot < n) {
+                const int32_t blk = a.page_table[(int64_t)b * a.max_pages + pg];
+                if (blk >= 0 && blk < a.num_blocks)
+                    r = (uint32_t)(((int64_t)blk * a.Hkv + h) * P + slot);
+                else if (slot == 0)
+                    report(a.status, RKV_DEV_BLOCK);
+            }
+        } else if (slot == 0) {
+            report(a.status, RKV_DEV_PAGE);
         }
         row_s[f] = r;
     }
@@ -164,19 +170,14 @@ attend_merge_kernel(int Hkv, int n_splits, const float *part, float *out) {
     out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
 }
 
-int env_int(const char *name, int dflt) {
-    const char *v = getenv(name);
-    return (v && *v) ? atoi(v) : dflt;
-}
-
 // Kernel variants: (waves per block, row loads per iteration, pipelined).
 constexpr int kVariantWaves[4] = {4, 8, 16, 16};
 
 template <typename T, int D, int G>
 int launch_t(const rkv_gqa &g, int B, const void *q, const rkv_paged_cache &c,
              const int32_t *seq_lens, const int32_t *page_idx, int k2, float scale, float *out,
-             void *ws, hipStream_t s) {
-    const AttendPlan pl = plan_attend(g, B, c.page_size, k2);
+             void *ws, const Knobs &kn, hipStream_t s) {
+    const AttendPlan pl = plan_attend(g, B, c.page_size, k2, kn);
     AttArgs a;
     a.Hkv = g.n_kv_heads;
     a.P = c.page_size;
@@ -191,6 +192,7 @@ int launch_t(const rkv_gqa &g, int B, const void *q, const rkv_paged_cache &c,
     a.qscale = scale * kLog2e;
     a.out = out;
     a.part = (float *)ws;
+    a.status = kn.status;
     dim3 grid(pl.n_splits, g.n_kv_heads, B);
     const T *kp = (const T *)c.k_pool, *vp = (const T *)c.v_pool, *qp = (const T *)q;
     switch (pl.variant) {
@@ -209,23 +211,23 @@ int launch_t(const rkv_gqa &g, int B, const void *q, const rkv_paged_cache &c,
 template <typename T, int D>
 int dispatch_g(const rkv_gqa &g, int B, const void *q, const rkv_paged_cache &c,
                const int32_t *seq_lens, const int32_t *page_idx, int k2, float scale, float *out,
-               void *ws, hipStream_t s) {
+               void *ws, const Knobs &kn, hipStream_t s) {
     switch (g.group) {
-        case 1: return launch_t<T, D, 1>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, s);
-        case 2: return launch_t<T, D, 2>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, s);
-        case 4: return launch_t<T, D, 4>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, s);
-        case 8: return launch_t<T, D, 8>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, s);
+        case 1: return launch_t<T, D, 1>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, kn, s);
+        case 2: return launch_t<T, D, 2>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, kn, s);
+        case 4: return launch_t<T, D, 4>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, kn, s);
+        case 8: return launch_t<T, D, 8>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, kn, s);
     }
     return RKV_EUNSUPPORTED;
 }
 
 }  // namespace
 
-AttendPlan plan_attend(const rkv_gqa &g, int B, int P, int k2) {
+AttendPlan plan_attend(const rkv_gqa &g, int B, int P, int k2, const Knobs &kn) {
     const int units = B * g.n_kv_heads;
     const int max_ppb = kMaxRows / P > 0 ? kMaxRows / P : 1;
     AttendPlan p;
-    int variant = env_int("RKV_ATTEND_VARIANT", -1);
+    int variant = kn.attend_variant - 1;  // option 1..4 -> kernel variant 0..3
     const bool wide_ok = g.group * g.head_dim <= 512;  // wide blocks keep G*D per wave in LDS
     if (variant < 0 || variant > 3) {
         // One wide block per (sequence, head) once the batch fills the chip;
@@ -234,7 +236,7 @@ AttendPlan plan_attend(const rkv_gqa &g, int B, int P, int k2) {
     }
     if (kVariantWaves[variant] > 4 && !wide_ok) variant = 0;
     const int waves = kVariantWaves[variant];
-    int ppb = env_int("RKV_ATTEND_PPB", 0);
+    int ppb = kn.attend_pages;
     if (ppb <= 0) {
         if (waves == 16) {
             ppb = k2;
@@ -256,8 +258,8 @@ AttendPlan plan_attend(const rkv_gqa &g, int B, int P, int k2) {
     return p;
 }
 
-size_t attend_ws_bytes(const rkv_gqa &g, int B, int P, int k2) {
-    const AttendPlan p = plan_attend(g, B, P, k2);
+size_t attend_ws_bytes(const rkv_gqa &g, int B, int P, int k2, const Knobs &kn) {
+    const AttendPlan p = plan_attend(g, B, P, k2, kn);
     if (p.n_splits == 1) return 0;
     return align_up((size_t)B * g.n_kv_heads * p.n_splits * g.group * (g.head_dim + 2) *
                     sizeof(float));
@@ -284,14 +286,14 @@ int launch_attend_merge(const rkv_gqa &g, int B, int n_splits, const float *part
 
 int launch_attend(const rkv_gqa &g, int dtype, int B, const void *q, const rkv_paged_cache &c,
                   const int32_t *seq_lens, const int32_t *page_idx, int k2, float scale,
-                  float *out, void *ws, hipStream_t s) {
+                  float *out, void *ws, const Knobs &kn, hipStream_t s) {
     const int d = g.head_dim;
     if (dtype == RKV_F32) {
-        if (d == 64) return dispatch_g<float, 64>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, s);
-        if (d == 128) return dispatch_g<float, 128>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, s);
+        if (d == 64) return dispatch_g<float, 64>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, kn, s);
+        if (d == 128) return dispatch_g<float, 128>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, kn, s);
     } else {
-        if (d == 64) return dispatch_g<uint16_t, 64>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, s);
-        if (d == 128) return dispatch_g<uint16_t, 128>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, s);
+        if (d == 64) return dispatch_g<uint16_t, 64>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, kn, s);
+        if (d == 128) return dispatch_g<uint16_t, 128>(g, B, q, c, seq_lens, page_idx, k2, scale, out, ws, kn, s);
     }
     return RKV_EUNSUPPORTED;
 }

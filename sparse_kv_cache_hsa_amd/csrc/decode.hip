@@ -22,8 +22,6 @@
 // the index outputs.  Two launches per step instead of four.  Otherwise the
 // standalone select (which appends the token) and attention kernels run in
 // sequence.
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "attend_core.h"
@@ -51,6 +49,7 @@ struct DecArgs {
     float *score_out;
     float *part;  // split-K: [B][Hkv][n_splits][G][D + 2] partials
     int pps;      // split-K: selected pages per split
+    int32_t *status;
 };
 
 template <typename T, int D, int G, bool SPLIT>
@@ -92,7 +91,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     const int P = a.P, k1 = a.k1, k2 = a.k2, max_pages = a.max_pages;
     const int64_t bh = (int64_t)b * a.Hkv + h;
     const int64_t cap = (int64_t)max_pages * P;
-    const int64_t n = min<int64_t>(max<int64_t>(a.seq_lens[b], 0), cap);
+    const int64_t n = clamp_rows(a.seq_lens[b], cap, (lead && h == 0 && tid == 0) ? a.status : nullptr);
     const int NP = (int)((n + P - 1) / P);
     T *sm_max = summ + bh * 2 * D * max_pages;
     T *sm_min = sm_max + (int64_t)D * max_pages;
@@ -157,6 +156,8 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             v_pool[dst] = vx;
             sm_max[im] = nmax;
             sm_min[im] = nmin;
+        } else if (lead && tid == 0) {
+            report(a.status, RKV_DEV_BLOCK);
         }
     };
     if (staged) {
@@ -234,7 +235,10 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         uint32_t r = kBadRow;
         if ((int64_t)pg * P + slot < n) {
             const int32_t blk = blk_s[pg];
-            if (blk >= 0 && blk < a.num_blocks) r = (uint32_t)(((int64_t)blk * a.Hkv + h) * P + slot);
+            if (blk >= 0 && blk < a.num_blocks)
+                r = (uint32_t)(((int64_t)blk * a.Hkv + h) * P + slot);
+            else if (slot == 0)
+                report(a.status, RKV_DEV_BLOCK);
         }
         row_s[f] = r;
     }
@@ -306,14 +310,10 @@ bool dispatch_g(int B, int nsp, const rkv_gqa &g, const DecArgs &a, const void *
     return false;
 }
 
-int env_int(const char *name, int dflt) {
-    const char *v = getenv(name);
-    return (v && *v) ? atoi(v) : dflt;
-}
-
-// Split-K shape: about kSplitBlocks blocks in all, whole pages per split.
-void split_counts(int units, int k2, int &n_splits, int &pages_per_split) {
-    const int target = env_int("RKV_SPLITK_BLOCKS", kSplitBlocks);
+// Split-K shape: about `target` blocks in all (0: kSplitBlocks), whole pages
+// per split.
+void split_counts(int units, int k2, int target, int &n_splits, int &pages_per_split) {
+    if (target <= 0) target = kSplitBlocks;
     int want = (target + units - 1) / units;
     if (want > k2) want = k2;
     if (want < 1) want = 1;
@@ -323,8 +323,9 @@ void split_counts(int units, int k2, int &n_splits, int &pages_per_split) {
 
 }  // namespace
 
-FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, int k1, int k2) {
-    FusedPlan p{0, 0, 0};
+FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, int k1, int k2,
+                     const Knobs &kn) {
+    FusedPlan p{RKV_FORM_STANDALONE, 0, 0};
     if (g.group * g.head_dim > 512 || g.group > 4) return p;
     if (max_pages > kFusedMaxPages || (int64_t)k2 * P > kFusedMaxRows) return p;
     const int units = B * g.n_kv_heads;
@@ -333,21 +334,21 @@ FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, i
     const int esz = dtype == RKV_F32 ? 4 : 2, V = 16 / esz;
     const bool stage_fits = max_pages <= kBlock &&
         (int64_t)2 * k1 * ((max_pages + V - 1) / V * V) * esz <= (int64_t)kStageBytes;
-    int mode = units >= 192 ? 1 : (stage_fits ? 2 : 0);
-    const int force = env_int("RKV_FUSED", -1);
-    if (force == 0 || force == 1) mode = force;
-    else if (force == 2 && stage_fits) mode = 2;
-    p.mode = mode;
-    if (mode == 2) split_counts(units, k2, p.n_splits, p.pages_per_split);
+    int form = units >= 192 ? RKV_FORM_FUSED : (stage_fits ? RKV_FORM_SPLITK : RKV_FORM_STANDALONE);
+    if (kn.form == RKV_FORM_STANDALONE || kn.form == RKV_FORM_FUSED) form = kn.form;
+    else if (kn.form == RKV_FORM_SPLITK) form = stage_fits ? RKV_FORM_SPLITK : RKV_FORM_STANDALONE;
+    p.form = form;
+    if (form == RKV_FORM_SPLITK)
+        split_counts(units, k2, kn.splitk_blocks, p.n_splits, p.pages_per_split);
     return p;
 }
 
-size_t fused_split_ws_bytes(const rkv_gqa &g, int B, int k2) {
-    // the split-K plan's partials for any dtype, k1 and RKV_FUSED setting:
-    // the same split count as plan_fused, whatever the batch
+size_t fused_split_ws_bytes(const rkv_gqa &g, int B, int k2, const Knobs &kn) {
+    // the split-K plan's partials for any dtype, k1 and form: the same split
+    // count as plan_fused, whatever the batch
     const int units = B * g.n_kv_heads;
     int nsp, pps;
-    split_counts(units, k2, nsp, pps);
+    split_counts(units, k2, kn.splitk_blocks, nsp, pps);
     return align_up((size_t)units * nsp * g.group * (g.head_dim + 2) * sizeof(float));
 }
 
@@ -355,7 +356,7 @@ int launch_decode_fused(const FusedPlan &pl, const rkv_gqa &g, int dtype, int B,
                         const void *k_new, const void *v_new, const rkv_paged_cache &c,
                         const int32_t *seq_lens, void *summaries, int k1, int k2, float scale,
                         float *out, int32_t *chan_idx, int32_t *page_idx, float *page_scores,
-                        float *part, size_t part_bytes, hipStream_t s) {
+                        float *part, size_t part_bytes, int32_t *status, hipStream_t s) {
     DecArgs a;
     a.Hkv = g.n_kv_heads;
     a.P = c.page_size;
@@ -372,7 +373,8 @@ int launch_decode_fused(const FusedPlan &pl, const rkv_gqa &g, int dtype, int B,
     a.score_out = page_scores;
     a.part = part;
     a.pps = pl.pages_per_split;
-    const int nsp = pl.mode == 2 ? pl.n_splits : 0;
+    a.status = status;
+    const int nsp = pl.form == RKV_FORM_SPLITK ? pl.n_splits : 0;
     if (nsp > 0 && (!part || (size_t)B * g.n_kv_heads * nsp * g.group * (g.head_dim + 2) *
                                      sizeof(float) > part_bytes))
         return RKV_EWORKSPACE;

@@ -484,7 +484,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256)
 gather_kernel(int Hkv, int64_t L_max, EvictSeq seq, const int32_t *kept, int64_t kept_stride,
               const T *k, const T *v, T *k_pool, T *v_pool, const int32_t *page_table, int P,
-              int max_pages, int64_t num_blocks) {
+              int max_pages, int64_t num_blocks, int32_t *status) {
     constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
     constexpr int RPB = 256 / CPR;
     const int b = blockIdx.z, h = blockIdx.y;
@@ -497,7 +497,10 @@ gather_kernel(int Hkv, int64_t L_max, EvictSeq seq, const int32_t *kept, int64_t
     const int32_t t = kept[bh * kept_stride + qrow];
     if (t < 0 || t >= L) return;
     const int32_t blk = page_table[(int64_t)b * max_pages + qrow / P];
-    if (blk < 0 || blk >= num_blocks) return;
+    if (blk < 0 || blk >= num_blocks) {
+        if (chunk == 0 && qrow % P == 0) report(status, RKV_DEV_BLOCK);
+        return;
+    }
     const int64_t src = (bh * L_max + t) * D;
     const int64_t dst = (((int64_t)blk * Hkv + h) * P + qrow % P) * D;
     ((uint4 *)(k_pool + dst))[chunk] = ((const uint4 *)(k + src))[chunk];
@@ -508,7 +511,7 @@ template <typename T, int D>
 int launch_t(const rkv_gqa &g, int B, const EvictSeq &seq, int64_t L_max, int w, int pool_kernel,
              float scale, const void *q_win, const void *k, const void *v,
              const rkv_paged_cache &c, void *summaries, int32_t *kept_idx, int keep_stride,
-             float *pooled, int32_t *seq_lens_out, void *ws, hipStream_t s) {
+             float *pooled, int32_t *seq_lens_out, void *ws, int32_t *status, hipStream_t s) {
     const EvictWs l = evict_layout(g, B, L_max, w);
     char *base = (char *)ws;
     float *Z = (float *)(base + l.z), *TM = (float *)(base + l.tm);
@@ -554,13 +557,13 @@ int launch_t(const rkv_gqa &g, int B, const EvictSeq &seq, int64_t L_max, int w,
         constexpr int RPB = 256 / (D * (int)sizeof(T) / 16);
         gather_kernel<T, D><<<dim3((int)((keep_rows + RPB - 1) / RPB), Hkv, B), 256, 0, s>>>(
             Hkv, L_max, seq, kept, kstride, (const T *)k, (const T *)v, (T *)c.k_pool,
-            (T *)c.v_pool, c.page_table, c.page_size, c.max_pages, c.num_blocks);
+            (T *)c.v_pool, c.page_table, c.page_size, c.max_pages, c.num_blocks, status);
     }
     int st = launch_status();
     if (st != RKV_OK) return st;
     if (summaries && keep_rows > 0)
         return launch_append(g, sizeof(T) == 4 ? RKV_F32 : RKV_BF16, B, c, nold, nnew,
-                             (int)keep_rows, nullptr, nullptr, summaries, s);
+                             (int)keep_rows, nullptr, nullptr, summaries, status, s);
     return RKV_OK;
 }
 
@@ -571,7 +574,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256)
 concat_kernel(int Hkv, int64_t L_max, ChunkSeq cs, const T *k_chunk, const T *v_chunk,
               int64_t C_max, const T *k_pool, const T *v_pool, const int32_t *page_table,
-              int P, int max_pages, int64_t num_blocks, T *k_cat, T *v_cat) {
+              int P, int max_pages, int64_t num_blocks, T *k_cat, T *v_cat, int32_t *status) {
     constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
     constexpr int RPB = 256 / CPR;
     const int b = blockIdx.z, h = blockIdx.y;
@@ -586,6 +589,8 @@ concat_kernel(int Hkv, int64_t L_max, ChunkSeq cs, const T *k_chunk, const T *v_
             const int64_t src = (((int64_t)blk * Hkv + h) * P + row % P) * D;
             kx = ((const uint4 *)(k_pool + src))[chunk];
             vx = ((const uint4 *)(v_pool + src))[chunk];
+        } else if (chunk == 0 && row % P == 0) {
+            report(status, RKV_DEV_BLOCK);
         }
     } else {
         const int64_t src = (bh * C_max + (row - cs.n_cached[b])) * D;
@@ -600,12 +605,13 @@ concat_kernel(int Hkv, int64_t L_max, ChunkSeq cs, const T *k_chunk, const T *v_
 template <typename T, int D>
 void launch_concat(const rkv_gqa &g, int B, const ChunkSeq &cs, int64_t L_max,
                    const void *k_chunk, const void *v_chunk, int64_t C_max,
-                   const rkv_paged_cache &c, void *k_cat, void *v_cat, hipStream_t s) {
+                   const rkv_paged_cache &c, void *k_cat, void *v_cat, int32_t *status,
+                   hipStream_t s) {
     constexpr int RPB = 256 / (D * (int)sizeof(T) / 16);
     concat_kernel<T, D><<<dim3((int)((L_max + RPB - 1) / RPB), g.n_kv_heads, B), 256, 0, s>>>(
         g.n_kv_heads, L_max, cs, (const T *)k_chunk, (const T *)v_chunk, C_max,
         (const T *)c.k_pool, (const T *)c.v_pool, c.page_table, c.page_size, c.max_pages,
-        c.num_blocks, (T *)k_cat, (T *)v_cat);
+        c.num_blocks, (T *)k_cat, (T *)v_cat, status);
 }
 
 size_t cat_bytes(const rkv_gqa &g, int B, int64_t L_max) {
@@ -624,24 +630,24 @@ int launch_evict_chunk(const rkv_gqa &g, int dtype, int B, const ChunkSeq &cs, c
                        const void *q_win, const void *k_chunk, const void *v_chunk,
                        const rkv_paged_cache &c, void *summaries, int32_t *kept_idx,
                        int keep_stride, float *pooled, int32_t *seq_lens_out, void *ws,
-                       hipStream_t s) {
+                       int32_t *status, hipStream_t s) {
     char *base = (char *)ws;
     void *k_cat = base, *v_cat = base + cat_bytes(g, B, L_max);
     void *ews = base + 2 * cat_bytes(g, B, L_max);
     const int d = g.head_dim;
     if (dtype == RKV_F32) {
-        if (d == 64) launch_concat<float, 64>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, s);
-        else if (d == 128) launch_concat<float, 128>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, s);
+        if (d == 64) launch_concat<float, 64>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, status, s);
+        else if (d == 128) launch_concat<float, 128>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, status, s);
         else return RKV_EUNSUPPORTED;
     } else {
-        if (d == 64) launch_concat<uint16_t, 64>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, s);
-        else if (d == 128) launch_concat<uint16_t, 128>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, s);
+        if (d == 64) launch_concat<uint16_t, 64>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, status, s);
+        else if (d == 128) launch_concat<uint16_t, 128>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, status, s);
         else return RKV_EUNSUPPORTED;
     }
     const int st = launch_status();
     if (st != RKV_OK) return st;
     return launch_evict(g, dtype, B, seq, L_max, w, pool_kernel, scale, q_win, k_cat, v_cat, c,
-                        summaries, kept_idx, keep_stride, pooled, seq_lens_out, ews, s);
+                        summaries, kept_idx, keep_stride, pooled, seq_lens_out, ews, status, s);
 }
 
 size_t evict_ws_bytes(const rkv_gqa &g, int B, int64_t L_max, int w) {
@@ -651,14 +657,14 @@ size_t evict_ws_bytes(const rkv_gqa &g, int B, int64_t L_max, int w) {
 int launch_evict(const rkv_gqa &g, int dtype, int B, const EvictSeq &seq, int64_t L_max, int w,
                  int pool_kernel, float scale, const void *q_win, const void *k, const void *v,
                  const rkv_paged_cache &c, void *summaries, int32_t *kept_idx, int keep_stride,
-                 float *pooled, int32_t *seq_lens_out, void *ws, hipStream_t s) {
+                 float *pooled, int32_t *seq_lens_out, void *ws, int32_t *status, hipStream_t s) {
     const int d = g.head_dim;
     if (dtype == RKV_F32) {
-        if (d == 64) return launch_t<float, 64>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, s);
-        if (d == 128) return launch_t<float, 128>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, s);
+        if (d == 64) return launch_t<float, 64>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, status, s);
+        if (d == 128) return launch_t<float, 128>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, status, s);
     } else {
-        if (d == 64) return launch_t<uint16_t, 64>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, s);
-        if (d == 128) return launch_t<uint16_t, 128>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, s);
+        if (d == 64) return launch_t<uint16_t, 64>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, status, s);
+        if (d == 128) return launch_t<uint16_t, 128>(g, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, c, summaries, kept_idx, keep_stride, pooled, seq_lens_out, ws, status, s);
     }
     return RKV_EUNSUPPORTED;
 }

@@ -51,6 +51,23 @@ int check_select_args(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
     return RKV_OK;
 }
 
+// Workspace of the decode family: [select candidates][attention partials]
+// [page_idx when the caller passes none][split-K partials], each part sized
+// for the plan the options give.
+struct HsaWs {
+    size_t select, attend, pages, split, total;
+};
+HsaWs hsa_ws(const rkv_gqa &g, int B, int P, int max_pages, int k2, const Knobs &kn) {
+    HsaWs w;
+    w.select = align_up(select_ws_bytes(g, B, max_pages, k2, kn));
+    w.attend = align_up(attend_ws_bytes(g, B, P, k2, kn));
+    w.pages = align_up((size_t)B * g.n_kv_heads * k2 * sizeof(int32_t));
+    w.split = fused_split_ws_bytes(g, B, k2, kn);
+    // +256 so that the size is never 0
+    w.total = w.select + w.attend + w.pages + w.split + 256;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -97,7 +114,8 @@ int rkv_prefill_evict(const rkv_gqa *g, int32_t dtype, int32_t B, const int32_t 
                       float scale, const void *q_win, const void *k, const void *v,
                       const rkv_paged_cache *cache, void *summaries, int32_t *kept_idx,
                       int32_t keep_stride, float *pooled_scores, int32_t *seq_lens_out,
-                      void *ws, size_t ws_bytes, void *stream) {
+                      void *ws, size_t ws_bytes, void *stream, const rkv_opts *opts) {
+    clear_pending_error();
     int st = check_gqa(g);
     if (st != RKV_OK) return st;
     if ((st = check_dtype(dtype)) != RKV_OK) return st;
@@ -127,7 +145,7 @@ int rkv_prefill_evict(const rkv_gqa *g, int32_t dtype, int32_t B, const int32_t 
     if (!ws || ws_bytes < need) return RKV_EWORKSPACE;
     return launch_evict(*g, dtype, B, seq, L_max, w, pool_kernel, scale, q_win, k, v, *cache,
                         summaries, kept_idx, keep_stride, pooled_scores, seq_lens_out, ws,
-                        (hipStream_t)stream);
+                        knobs_of(opts).status, (hipStream_t)stream);
 }
 
 size_t rkv_prefill_evict_chunk_workspace_bytes(const rkv_gqa *g, int32_t B, int64_t L_max,
@@ -143,7 +161,8 @@ int rkv_prefill_evict_chunk(const rkv_gqa *g, int32_t dtype, int32_t B,
                             const void *k_chunk, const void *v_chunk,
                             const rkv_paged_cache *cache, void *summaries, int32_t *kept_idx,
                             int32_t keep_stride, float *pooled_scores, int32_t *seq_lens_out,
-                            void *ws, size_t ws_bytes, void *stream) {
+                            void *ws, size_t ws_bytes, void *stream, const rkv_opts *opts) {
+    clear_pending_error();
     int st = check_gqa(g);
     if (st != RKV_OK) return st;
     if ((st = check_dtype(dtype)) != RKV_OK) return st;
@@ -183,13 +202,16 @@ int rkv_prefill_evict_chunk(const rkv_gqa *g, int32_t dtype, int32_t B,
     if (!ws || ws_bytes < need) return RKV_EWORKSPACE;
     return launch_evict_chunk(*g, dtype, B, cs, seq, L_max, C_max, w, pool_kernel, scale, q_win,
                               k_chunk, v_chunk, *cache, summaries, kept_idx, keep_stride,
-                              pooled_scores, seq_lens_out, ws, (hipStream_t)stream);
+                              pooled_scores, seq_lens_out, ws, knobs_of(opts).status,
+                              (hipStream_t)stream);
 }
 
 int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,
                          const rkv_paged_cache *cache, const int32_t *n_old,
                          const int32_t *n_new, int32_t max_new_rows, const void *k_src,
-                         const void *v_src, void *summaries, void *stream) {
+                         const void *v_src, void *summaries, void *stream,
+                         const rkv_opts *opts) {
+    clear_pending_error();
     int st = check_gqa(g);
     if (st != RKV_OK) return st;
     if ((st = check_dtype(dtype)) != RKV_OK) return st;
@@ -200,69 +222,70 @@ int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,
     const int64_t pages = (int64_t)(max_new_rows + cache->page_size - 1) / cache->page_size + 1;
     if (pages > 0x7fffffff) return RKV_EINVAL;
     return launch_append(*g, dtype, B, *cache, n_old, n_new, max_new_rows, k_src, v_src,
-                         summaries, (hipStream_t)stream);
+                         summaries, knobs_of(opts).status, (hipStream_t)stream);
 }
 
 size_t rkv_hsa_workspace_bytes(const rkv_gqa *g, int32_t B, int32_t page_size,
-                               int32_t max_pages, int32_t k1, int32_t k2) {
+                               int32_t max_pages, int32_t k1, int32_t k2,
+                               const rkv_opts *opts) {
     (void)k1;
     if (check_gqa(g) != RKV_OK || B < 1 || page_size < 1 || max_pages < 1 || k2 < 1) return 0;
-    // select candidates, attention partials, and page_idx when the caller
-    // of rkv_hsa_decode passes none; +256 so the result is never 0.
-    return align_up(select_ws_bytes(*g, B, max_pages, k2)) +
-           align_up(attend_ws_bytes(*g, B, page_size, k2)) +
-           align_up((size_t)B * g->n_kv_heads * k2 * sizeof(int32_t)) +
-           fused_split_ws_bytes(*g, B, k2) + 256;
+    return hsa_ws(*g, B, page_size, max_pages, k2, knobs_of(opts)).total;
 }
 
 int rkv_hsa_select(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                    const int32_t *seq_lens, int32_t page_size, int32_t max_pages,
                    const void *summaries, int32_t k1, int32_t k2, int32_t *chan_idx,
                    int32_t *page_idx, float *page_scores, void *ws, size_t ws_bytes,
-                   void *stream) {
+                   void *stream, const rkv_opts *opts) {
+    clear_pending_error();
     int st = check_select_args(g, dtype, B, q, seq_lens, page_size, max_pages, k1, k2);
     if (st != RKV_OK) return st;
     if (!summaries || !page_idx) return RKV_EINVAL;
-    if (!ws || ws_bytes < rkv_hsa_workspace_bytes(g, B, page_size, max_pages, k1, k2))
+    const Knobs kn = knobs_of(opts);
+    if (!ws || ws_bytes < hsa_ws(*g, B, page_size, max_pages, k2, kn).total)
         return RKV_EWORKSPACE;
     return launch_select(*g, dtype, B, q, seq_lens, page_size, max_pages, (void *)summaries, k1,
-                         k2, chan_idx, page_idx, page_scores, ws, nullptr, nullptr, nullptr,
+                         k2, chan_idx, page_idx, page_scores, ws, nullptr, nullptr, nullptr, kn,
                          (hipStream_t)stream);
 }
 
 int rkv_hsa_attend(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                    const rkv_paged_cache *cache, const int32_t *seq_lens,
                    const int32_t *page_idx, int32_t k2, float scale, float *out, void *ws,
-                   size_t ws_bytes, void *stream) {
+                   size_t ws_bytes, void *stream, const rkv_opts *opts) {
+    clear_pending_error();
     int st = check_gqa(g);
     if (st != RKV_OK) return st;
     if ((st = check_cache(cache)) != RKV_OK) return st;
     st = check_select_args(g, dtype, B, q, seq_lens, cache->page_size, cache->max_pages, 1, k2);
     if (st != RKV_OK) return st;
     if (!page_idx || !out || !(scale > 0.0f) || !isfinite(scale)) return RKV_EINVAL;
-    const size_t need = rkv_hsa_workspace_bytes(g, B, cache->page_size, cache->max_pages, 1, k2);
-    if (!ws || ws_bytes < need) return RKV_EWORKSPACE;
-    char *base = (char *)ws + align_up(select_ws_bytes(*g, B, cache->max_pages, k2));
-    return launch_attend(*g, dtype, B, q, *cache, seq_lens, page_idx, k2, scale, out, base,
-                         (hipStream_t)stream);
+    const Knobs kn = knobs_of(opts);
+    const HsaWs w = hsa_ws(*g, B, cache->page_size, cache->max_pages, k2, kn);
+    if (!ws || ws_bytes < w.total) return RKV_EWORKSPACE;
+    return launch_attend(*g, dtype, B, q, *cache, seq_lens, page_idx, k2, scale, out,
+                         (char *)ws + w.select, kn, (hipStream_t)stream);
 }
 
 int rkv_decode_mode(const rkv_gqa *g, int32_t dtype, int32_t B, int32_t page_size,
-                    int32_t max_pages, int32_t k1, int32_t k2) {
+                    int32_t max_pages, int32_t k1, int32_t k2, const rkv_opts *opts) {
     int st = check_gqa(g);
     if (st != RKV_OK) return st;
     if (dtype != RKV_F32 && dtype != RKV_BF16) return RKV_EUNSUPPORTED;
     if (B < 1 || page_size < 1 || max_pages < 1 || k1 < 1 || k1 > g->head_dim || k2 < 1 ||
         k2 > RKV_MAX_K2)
         return RKV_EINVAL;
-    return plan_fused(*g, dtype, B, page_size, max_pages, k1, k2).mode;
+    return plan_fused(*g, dtype, B, page_size, max_pages, k1, k2, knobs_of(opts)).form;
 }
 
 int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                     const void *k_new, const void *v_new, const rkv_paged_cache *cache,
                     const int32_t *seq_lens, void *summaries, int32_t k1, int32_t k2,
                     float scale, float *out, int32_t *chan_idx, int32_t *page_idx,
-                    float *page_scores, void *ws, size_t ws_bytes, void *stream) {
+                    float *page_scores, void *ws, size_t ws_bytes, void *stream,
+                    const rkv_opts *opts) {
+    clear_pending_error();
     int st = check_gqa(g);
     if (st != RKV_OK) return st;
     if ((st = check_cache(cache)) != RKV_OK) return st;
@@ -270,38 +293,35 @@ int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
     if (st != RKV_OK) return st;
     if (!summaries || !out || !(scale > 0.0f) || !isfinite(scale)) return RKV_EINVAL;
     if ((k_new == nullptr) != (v_new == nullptr)) return RKV_EINVAL;
-    const size_t need = rkv_hsa_workspace_bytes(g, B, cache->page_size, cache->max_pages, k1, k2);
-    if (!ws || ws_bytes < need) return RKV_EWORKSPACE;
+    const Knobs kn = knobs_of(opts);
+    const HsaWs w = hsa_ws(*g, B, cache->page_size, cache->max_pages, k2, kn);
+    if (!ws || ws_bytes < w.total) return RKV_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
-    const FusedPlan fp = plan_fused(*g, dtype, B, cache->page_size, cache->max_pages, k1, k2);
-    if (fp.mode != 0) {
-        const size_t off = align_up(select_ws_bytes(*g, B, cache->max_pages, k2)) +
-                           align_up(attend_ws_bytes(*g, B, cache->page_size, k2)) +
-                           align_up((size_t)B * g->n_kv_heads * k2 * sizeof(int32_t));
+    char *base = (char *)ws;
+    const FusedPlan fp = plan_fused(*g, dtype, B, cache->page_size, cache->max_pages, k1, k2, kn);
+    if (fp.form != RKV_FORM_STANDALONE) {
+        const size_t off = w.select + w.attend + w.pages;
         return launch_decode_fused(fp, *g, dtype, B, q, k_new, v_new, *cache, seq_lens, summaries,
                                    k1, k2, scale, out, chan_idx, page_idx, page_scores,
-                                   (float *)((char *)ws + off), ws_bytes - off, s);
+                                   (float *)(base + off), ws_bytes - off, kn.status, s);
     }
-    if (!page_idx) {
-        page_idx = (int32_t *)((char *)ws + align_up(select_ws_bytes(*g, B, cache->max_pages, k2)) +
-                               align_up(attend_ws_bytes(*g, B, cache->page_size, k2)));
-    }
+    if (!page_idx) page_idx = (int32_t *)(base + w.select + w.attend);
     // the select kernel appends the new token itself
     st = launch_select(*g, dtype, B, q, seq_lens, cache->page_size, cache->max_pages, summaries,
-                       k1, k2, chan_idx, page_idx, page_scores, ws, k_new, v_new, cache, s);
+                       k1, k2, chan_idx, page_idx, page_scores, ws, k_new, v_new, cache, kn, s);
     if (st != RKV_OK) return st;
-    char *base = (char *)ws + align_up(select_ws_bytes(*g, B, cache->max_pages, k2));
-    return launch_attend(*g, dtype, B, q, *cache, seq_lens, page_idx, k2, scale, out, base, s);
+    return launch_attend(*g, dtype, B, q, *cache, seq_lens, page_idx, k2, scale, out,
+                         base + w.select, kn, s);
 }
 
 int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                    const rkv_paged_cache *cache, const int32_t *seq_lens, const void *summaries,
                    int32_t k1, int32_t k2, float scale, float *out, int32_t *chan_idx,
                    int32_t *page_idx, float *page_scores, void *ws, size_t ws_bytes,
-                   void *stream) {
+                   void *stream, const rkv_opts *opts) {
     return rkv_decode_step(g, dtype, B, q, nullptr, nullptr, cache, seq_lens, (void *)summaries,
                            k1, k2, scale, out, chan_idx, page_idx, page_scores, ws, ws_bytes,
-                           stream);
+                           stream, opts);
 }
 
 }  // extern "C"

@@ -292,8 +292,51 @@ __device__ __forceinline__ float exp2_diff(float a, float b) {
 }
 
 // ---- launch helpers ------------------------------------------------------
+// Entry points call clear_pending_error() before enqueuing anything, so the
+// error launch_status() reads after their launches is their own.
+inline void clear_pending_error() { (void)hipGetLastError(); }
 inline int launch_status() {
     return hipGetLastError() == hipSuccess ? RKV_OK : RKV_EHIP;
+}
+
+// Reports a device-side input the kernels had to clamp or skip (RKV_DEV_*
+// flags) in the caller's optional status word.
+__device__ __forceinline__ void report(int32_t *status, int32_t flag) {
+    if (status) atomicOr(status, flag);
+}
+
+// Row count of a sequence from device memory, clamped to [0, cap]; a value
+// outside that range is reported.
+__device__ __forceinline__ int64_t clamp_rows(int32_t raw, int64_t cap, int32_t *status) {
+    if (raw < 0 || (int64_t)raw > cap) {
+        report(status, RKV_DEV_LENGTH);
+        return raw < 0 ? 0 : cap;
+    }
+    return raw;
+}
+
+// The execution options with every automatic choice still open (0 = auto).
+struct Knobs {
+    int form = RKV_FORM_AUTO;
+    int splitk_blocks = 0;
+    int select_chunk = 0;
+    int select_radix = 0;
+    int attend_variant = 0;
+    int attend_pages = 0;
+    int32_t *status = nullptr;
+};
+inline Knobs knobs_of(const rkv_opts *o) {
+    Knobs k;
+    if (o) {
+        k.form = o->form;
+        k.splitk_blocks = o->splitk_blocks;
+        k.select_chunk = o->select_chunk;
+        k.select_radix = o->select_radix;
+        k.attend_variant = o->attend_variant;
+        k.attend_pages = o->attend_pages;
+        k.status = o->status;
+    }
+    return k;
 }
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
@@ -302,22 +345,23 @@ inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 // n_old == nullptr appends exactly one row per sequence, ending at n_new.
 int launch_append(const rkv_gqa &g, int dtype, int B, const rkv_paged_cache &c,
                   const int32_t *n_old, const int32_t *n_new, int max_new_rows,
-                  const void *k_src, const void *v_src, void *summaries, hipStream_t s);
+                  const void *k_src, const void *v_src, void *summaries, int32_t *status,
+                  hipStream_t s);
 
 struct SelectPlan {
     int chunk_pages;  // pages scored per block
     int n_chunks;     // blocks per (sequence, KV head)
     int sorted;       // 0, or the keys per lane (1, 2, 4) of the rank-ordered list merge
 };
-SelectPlan plan_select(const rkv_gqa &g, int B, int max_pages, int k2);
-size_t select_ws_bytes(const rkv_gqa &g, int B, int max_pages, int k2);
+SelectPlan plan_select(const rkv_gqa &g, int B, int max_pages, int k2, const Knobs &kn);
+size_t select_ws_bytes(const rkv_gqa &g, int B, int max_pages, int k2, const Knobs &kn);
 // With k_new/v_new and cache given (a decode step), the block whose chunk
 // holds row n-1 also appends it: K/V row into the cache, page summary folded.
 int launch_select(const rkv_gqa &g, int dtype, int B, const void *q, const int32_t *seq_lens,
                   int P, int max_pages, void *summaries, int k1, int k2,
                   int32_t *chan_idx, int32_t *page_idx, float *page_scores, void *ws,
                   const void *k_new, const void *v_new, const rkv_paged_cache *cache,
-                  hipStream_t s);
+                  const Knobs &kn, hipStream_t s);
 
 struct AttendPlan {
     int pages_per_block;
@@ -325,31 +369,33 @@ struct AttendPlan {
     int waves;    // waves per block
     int variant;  // kernel variant (waves, loads per iteration, pipelining)
 };
-AttendPlan plan_attend(const rkv_gqa &g, int B, int P, int k2);
-size_t attend_ws_bytes(const rkv_gqa &g, int B, int P, int k2);
+AttendPlan plan_attend(const rkv_gqa &g, int B, int P, int k2, const Knobs &kn);
+size_t attend_ws_bytes(const rkv_gqa &g, int B, int P, int k2, const Knobs &kn);
 int launch_attend(const rkv_gqa &g, int dtype, int B, const void *q,
                   const rkv_paged_cache &c, const int32_t *seq_lens, const int32_t *page_idx,
-                  int k2, float scale, float *out, void *ws, hipStream_t s);
+                  int k2, float scale, float *out, void *ws, const Knobs &kn, hipStream_t s);
 
 // Combines split-K attention partials [B][Hkv][n_splits][G][d + 2] in split
 // order into out [B][Hq][d].
 int launch_attend_merge(const rkv_gqa &g, int B, int n_splits, const float *part, float *out,
                         hipStream_t s);
 
-// How rkv_decode_step runs: mode 0 = the standalone kernels, 1 = the fused
-// kernel with one block per (sequence, KV head), 2 = the fused kernel split
-// K-wise over n_splits blocks per unit (pages_per_split selected pages each)
-// plus the attention merge.
+// How rkv_decode_step runs: form RKV_FORM_STANDALONE (the standalone
+// kernels), RKV_FORM_FUSED (the fused kernel with one block per (sequence,
+// KV head)) or RKV_FORM_SPLITK (the fused kernel split K-wise over n_splits
+// blocks per unit, pages_per_split selected pages each, plus the attention
+// merge).
 struct FusedPlan {
-    int mode, n_splits, pages_per_split;
+    int form, n_splits, pages_per_split;
 };
-FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, int k1, int k2);
-size_t fused_split_ws_bytes(const rkv_gqa &g, int B, int k2);
+FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, int k1, int k2,
+                     const Knobs &kn);
+size_t fused_split_ws_bytes(const rkv_gqa &g, int B, int k2, const Knobs &kn);
 int launch_decode_fused(const FusedPlan &pl, const rkv_gqa &g, int dtype, int B, const void *q,
                         const void *k_new, const void *v_new, const rkv_paged_cache &c,
                         const int32_t *seq_lens, void *summaries, int k1, int k2, float scale,
                         float *out, int32_t *chan_idx, int32_t *page_idx, float *page_scores,
-                        float *part, size_t part_bytes, hipStream_t s);
+                        float *part, size_t part_bytes, int32_t *status, hipStream_t s);
 
 struct EvictSeq {
     int32_t L[RKV_MAX_EVICT_BATCH];
@@ -366,11 +412,11 @@ int launch_evict_chunk(const rkv_gqa &g, int dtype, int B, const ChunkSeq &cs, c
                        const void *q_win, const void *k_chunk, const void *v_chunk,
                        const rkv_paged_cache &c, void *summaries, int32_t *kept_idx,
                        int keep_stride, float *pooled, int32_t *seq_lens_out, void *ws,
-                       hipStream_t s);
+                       int32_t *status, hipStream_t s);
 int launch_evict(const rkv_gqa &g, int dtype, int B, const EvictSeq &seq, int64_t L_max,
                  int w, int pool_kernel, float scale, const void *q_win, const void *k,
                  const void *v, const rkv_paged_cache &c, void *summaries,
                  int32_t *kept_idx, int keep_stride, float *pooled, int32_t *seq_lens_out,
-                 void *ws, hipStream_t s);
+                 void *ws, int32_t *status, hipStream_t s);
 
 }  // namespace rkv

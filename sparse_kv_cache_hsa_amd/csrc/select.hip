@@ -20,8 +20,6 @@
 //                   chunks' candidates, which are stored chunk-major in
 //                   ascending page order, so the position order equals the
 //                   page order for tie-breaking.
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "select_core.h"
@@ -53,6 +51,7 @@ struct SelArgs {
     float *score_out;
     uint32_t *cand_key;
     int32_t *cand_page;
+    int32_t *status;
 };
 
 // ---- bitonic lists held by one wave ----------------------------------------
@@ -159,7 +158,7 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
     const int P = a.P, k1 = a.k1, k2 = a.k2;
     const int64_t bh = (int64_t)b * a.Hkv + h;
     const int64_t cap = (int64_t)a.max_pages * P;
-    const int64_t n = min<int64_t>(max<int64_t>(a.seq_lens[b], 0), cap);
+    const int64_t n = clamp_rows(a.seq_lens[b], cap, (ck == 0 && h == 0 && tid == 0) ? a.status : nullptr);
     const int NP = (int)((n + P - 1) / P);
 
     const int p0 = ck * a.chunk;
@@ -192,6 +191,8 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
             ((T *)a.v_pool)[dst] = ((const T *)a.v_new)[bh * D + tid];
             smax[im] = nmax;
             smin[im] = nmin;
+        } else if (tid == 0) {
+            report(a.status, RKV_DEV_BLOCK);
         }
     }
     lds_barrier();
@@ -402,16 +403,11 @@ bool dispatch_g(int G, dim3 grid, bool sorted, hipStream_t s, const SelArgs &a, 
     return false;
 }
 
-int env_int(const char *name, int dflt) {
-    const char *v = getenv(name);
-    return (v && *v) ? atoi(v) : dflt;
-}
-
 }  // namespace
 
-SelectPlan plan_select(const rkv_gqa &g, int B, int max_pages, int k2) {
+SelectPlan plan_select(const rkv_gqa &g, int B, int max_pages, int k2, const Knobs &kn) {
     const int units = B * g.n_kv_heads;
-    int chunk = env_int("RKV_SELECT_CHUNK", 0);
+    int chunk = kn.select_chunk;
     if (chunk <= 0) {
         // One block per (sequence, head) when the batch fills the chip;
         // otherwise aim for >= 512 blocks of >= 128 pages each.
@@ -429,7 +425,7 @@ SelectPlan plan_select(const rkv_gqa &g, int B, int max_pages, int k2) {
     p.n_chunks = (max_pages + chunk - 1) / chunk;
     if (p.n_chunks < 1) p.n_chunks = 1;
     p.sorted = 0;
-    if (p.n_chunks > 1 && k2 <= 4 * kWave && env_int("RKV_SELECT_SORTED", 1) != 0) {
+    if (p.n_chunks > 1 && k2 <= 4 * kWave && kn.select_radix == 0) {
         // elements per lane of a merge list: k2 rounded up to 64, 128 or 256
         const int E = k2 <= kWave ? 1 : (k2 <= 2 * kWave ? 2 : 4);
         const int sc = chunk < kSortedChunk ? chunk : kSortedChunk;
@@ -443,8 +439,8 @@ SelectPlan plan_select(const rkv_gqa &g, int B, int max_pages, int k2) {
     return p;
 }
 
-size_t select_ws_bytes(const rkv_gqa &g, int B, int max_pages, int k2) {
-    const SelectPlan p = plan_select(g, B, max_pages, k2);
+size_t select_ws_bytes(const rkv_gqa &g, int B, int max_pages, int k2, const Knobs &kn) {
+    const SelectPlan p = plan_select(g, B, max_pages, k2, kn);
     if (p.n_chunks == 1) return 0;
     const size_t m = (size_t)B * g.n_kv_heads * p.n_chunks * k2;
     return align_up(m * sizeof(uint32_t)) + align_up(m * sizeof(int32_t));
@@ -454,8 +450,8 @@ int launch_select(const rkv_gqa &g, int dtype, int B, const void *q, const int32
                   int P, int max_pages, void *summaries, int k1, int k2,
                   int32_t *chan_idx, int32_t *page_idx, float *page_scores, void *ws,
                   const void *k_new, const void *v_new, const rkv_paged_cache *cache,
-                  hipStream_t s) {
-    const SelectPlan pl = plan_select(g, B, max_pages, k2);
+                  const Knobs &kn, hipStream_t s) {
+    const SelectPlan pl = plan_select(g, B, max_pages, k2, kn);
     SelArgs a;
     a.Hkv = g.n_kv_heads;
     a.P = P;
@@ -476,6 +472,7 @@ int launch_select(const rkv_gqa &g, int dtype, int B, const void *q, const int32
     a.v_pool = cache ? cache->v_pool : nullptr;
     a.page_table = cache ? cache->page_table : nullptr;
     a.num_blocks = cache ? cache->num_blocks : 0;
+    a.status = kn.status;
     if (pl.n_chunks > 1) {
         const size_t m = (size_t)B * g.n_kv_heads * pl.n_chunks * k2;
         a.cand_key = (uint32_t *)ws;

@@ -19,19 +19,25 @@ template <typename T, int D>
 __global__ void __launch_bounds__(D)
 append_kernel(int Hkv, int P, int max_pages, int64_t num_blocks, const int32_t *page_table,
               T *k_pool, T *v_pool, const int32_t *n_old, const int32_t *n_new, int max_new,
-              const T *k_src, const T *v_src, T *summ) {
+              const T *k_src, const T *v_src, T *summ, int32_t *status) {
     const int b = blockIdx.z, h = blockIdx.y, c = threadIdx.x;
     const int64_t cap = (int64_t)max_pages * P;
-    const int64_t o_in = n_old ? (int64_t)n_old[b] : (int64_t)n_new[b] - 1;
-    const int64_t o = min<int64_t>(max<int64_t>(o_in, 0), cap);
-    int64_t e = min<int64_t>(max<int64_t>(n_new[b], 0), cap);
+    // one thread per sequence reports out-of-range row counts
+    int32_t *st = (blockIdx.x == 0 && h == 0 && c == 0) ? status : nullptr;
+    const int64_t e_raw = n_new[b];
+    int64_t e = clamp_rows(n_new[b], cap, st);
+    const int64_t o = n_old ? clamp_rows(n_old[b], cap, st)
+                            : min<int64_t>(max<int64_t>(e_raw - 1, 0), cap);
     e = min<int64_t>(e, o + max_new);
     if (e <= o) return;
     const int64_t pg = o / P + blockIdx.x;
     const int64_t r0 = pg * P;
     if (r0 >= e) return;
     const int32_t blk = page_table[(int64_t)b * max_pages + pg];
-    if (blk < 0 || blk >= num_blocks) return;
+    if (blk < 0 || blk >= num_blocks) {
+        if (c == 0) report(status, RKV_DEV_BLOCK);
+        return;
+    }
     const int64_t rs = max<int64_t>(r0, o), re = min<int64_t>(r0 + P, e);
 
     T *kp = k_pool + ((int64_t)blk * Hkv + h) * P * D;
@@ -73,12 +79,13 @@ append_kernel(int Hkv, int P, int max_pages, int64_t num_blocks, const int32_t *
 template <typename T, int D>
 int launch_t(const rkv_gqa &g, int B, const rkv_paged_cache &c, const int32_t *n_old,
              const int32_t *n_new, int max_new, const void *k_src, const void *v_src,
-             void *summ, hipStream_t s) {
+             void *summ, int32_t *status, hipStream_t s) {
     const int pages = (max_new + c.page_size - 1) / c.page_size + 1;
     dim3 grid(pages, g.n_kv_heads, B);
     append_kernel<T, D><<<grid, D, 0, s>>>(
         g.n_kv_heads, c.page_size, c.max_pages, c.num_blocks, c.page_table, (T *)c.k_pool,
-        (T *)c.v_pool, n_old, n_new, max_new, (const T *)k_src, (const T *)v_src, (T *)summ);
+        (T *)c.v_pool, n_old, n_new, max_new, (const T *)k_src, (const T *)v_src, (T *)summ,
+        status);
     return launch_status();
 }
 
@@ -86,14 +93,15 @@ int launch_t(const rkv_gqa &g, int B, const rkv_paged_cache &c, const int32_t *n
 
 int launch_append(const rkv_gqa &g, int dtype, int B, const rkv_paged_cache &c,
                   const int32_t *n_old, const int32_t *n_new, int max_new_rows,
-                  const void *k_src, const void *v_src, void *summaries, hipStream_t s) {
+                  const void *k_src, const void *v_src, void *summaries, int32_t *status,
+                  hipStream_t s) {
     const int d = g.head_dim;
     if (dtype == RKV_F32) {
-        if (d == 64) return launch_t<float, 64>(g, B, c, n_old, n_new, max_new_rows, k_src, v_src, summaries, s);
-        if (d == 128) return launch_t<float, 128>(g, B, c, n_old, n_new, max_new_rows, k_src, v_src, summaries, s);
+        if (d == 64) return launch_t<float, 64>(g, B, c, n_old, n_new, max_new_rows, k_src, v_src, summaries, status, s);
+        if (d == 128) return launch_t<float, 128>(g, B, c, n_old, n_new, max_new_rows, k_src, v_src, summaries, status, s);
     } else {
-        if (d == 64) return launch_t<uint16_t, 64>(g, B, c, n_old, n_new, max_new_rows, k_src, v_src, summaries, s);
-        if (d == 128) return launch_t<uint16_t, 128>(g, B, c, n_old, n_new, max_new_rows, k_src, v_src, summaries, s);
+        if (d == 64) return launch_t<uint16_t, 64>(g, B, c, n_old, n_new, max_new_rows, k_src, v_src, summaries, status, s);
+        if (d == 128) return launch_t<uint16_t, 128>(g, B, c, n_old, n_new, max_new_rows, k_src, v_src, summaries, status, s);
     }
     return RKV_EUNSUPPORTED;
 }

@@ -28,6 +28,13 @@ RKV_F32 = 0
 RKV_BF16 = 1
 RKV_MAX_K2 = 1024
 RKV_MAX_EVICT_BATCH = 128
+RKV_FORM_AUTO = 0
+RKV_FORM_STANDALONE = 1
+RKV_FORM_FUSED = 2
+RKV_FORM_SPLITK = 3
+RKV_DEV_LENGTH = 1
+RKV_DEV_BLOCK = 2
+RKV_DEV_PAGE = 4
 
 EXPORTED = (
     "rkv_status_string", "rkv_build_id", "rkv_split_ratio",
@@ -55,6 +62,28 @@ class rkv_paged_cache(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
 
 
+class rkv_opts(ctypes.Structure):
+    _fields_ = [("form", ctypes.c_int32), ("splitk_blocks", ctypes.c_int32),
+                ("select_chunk", ctypes.c_int32), ("select_radix", ctypes.c_int32),
+                ("attend_variant", ctypes.c_int32), ("attend_pages", ctypes.c_int32),
+                ("status", ctypes.c_void_p)]
+
+
+def make_opts(form: int = RKV_FORM_AUTO, splitk_blocks: int = 0, select_chunk: int = 0,
+              select_radix: int = 0, attend_variant: int = 0, attend_pages: int = 0,
+              status: torch.Tensor | None = None) -> rkv_opts:
+    """Execution options (include/rkv.h rkv_opts).  status: optional device
+    int32 tensor of one element that receives RKV_DEV_* flags."""
+    if status is not None:
+        _need(status, "status", torch.int32)
+    return rkv_opts(int(form), int(splitk_blocks), int(select_chunk), int(select_radix),
+                    int(attend_variant), int(attend_pages), _ptr(status))
+
+
+def _opt(o: rkv_opts | None):
+    return None if o is None else ctypes.byref(o)
+
+
 _LOCK = threading.Lock()
 _LIB = None
 
@@ -72,7 +101,7 @@ def load_library(path: str | None = None, check_build_id: bool = True):
         i32, i64, f32, f64, vp, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                       ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t)
         P = ctypes.POINTER
-        G, C = P(rkv_gqa), P(rkv_paged_cache)
+        G, C, O = P(rkv_gqa), P(rkv_paged_cache), P(rkv_opts)
         lib.rkv_status_string.argtypes = [ctypes.c_int]
         lib.rkv_status_string.restype = ctypes.c_char_p
         lib.rkv_build_id.argtypes = []
@@ -82,30 +111,30 @@ def load_library(path: str | None = None, check_build_id: bool = True):
         lib.rkv_prefill_evict_workspace_bytes.argtypes = [G, i32, i64, i32]
         lib.rkv_prefill_evict_workspace_bytes.restype = sz
         lib.rkv_prefill_evict.argtypes = [G, i32, i32, P(i32), P(i32), i64, i32, i32, f32, vp,
-                                          vp, vp, C, vp, vp, i32, vp, vp, vp, sz, vp]
+                                          vp, vp, C, vp, vp, i32, vp, vp, vp, sz, vp, O]
         lib.rkv_prefill_evict.restype = ctypes.c_int
         lib.rkv_prefill_evict_chunk_workspace_bytes.argtypes = [G, i32, i64, i32]
         lib.rkv_prefill_evict_chunk_workspace_bytes.restype = sz
         lib.rkv_prefill_evict_chunk.argtypes = [G, i32, i32, P(i32), P(i32), P(i32), i64, i32,
                                                 i32, f32, vp, vp, vp, C, vp, vp, i32, vp, vp,
-                                                vp, sz, vp]
+                                                vp, sz, vp, O]
         lib.rkv_prefill_evict_chunk.restype = ctypes.c_int
-        lib.rkv_append_summaries.argtypes = [G, i32, i32, C, vp, vp, i32, vp, vp, vp, vp]
+        lib.rkv_append_summaries.argtypes = [G, i32, i32, C, vp, vp, i32, vp, vp, vp, vp, O]
         lib.rkv_append_summaries.restype = ctypes.c_int
-        lib.rkv_hsa_workspace_bytes.argtypes = [G, i32, i32, i32, i32, i32]
+        lib.rkv_hsa_workspace_bytes.argtypes = [G, i32, i32, i32, i32, i32, O]
         lib.rkv_hsa_workspace_bytes.restype = sz
-        lib.rkv_decode_mode.argtypes = [G, i32, i32, i32, i32, i32, i32]
+        lib.rkv_decode_mode.argtypes = [G, i32, i32, i32, i32, i32, i32, O]
         lib.rkv_decode_mode.restype = ctypes.c_int
         lib.rkv_hsa_select.argtypes = [G, i32, i32, vp, vp, i32, i32, vp, i32, i32, vp, vp, vp,
-                                       vp, sz, vp]
+                                       vp, sz, vp, O]
         lib.rkv_hsa_select.restype = ctypes.c_int
-        lib.rkv_hsa_attend.argtypes = [G, i32, i32, vp, C, vp, vp, i32, f32, vp, vp, sz, vp]
+        lib.rkv_hsa_attend.argtypes = [G, i32, i32, vp, C, vp, vp, i32, f32, vp, vp, sz, vp, O]
         lib.rkv_hsa_attend.restype = ctypes.c_int
         lib.rkv_hsa_decode.argtypes = [G, i32, i32, vp, C, vp, vp, i32, i32, f32, vp, vp, vp,
-                                       vp, vp, sz, vp]
+                                       vp, vp, sz, vp, O]
         lib.rkv_hsa_decode.restype = ctypes.c_int
         lib.rkv_decode_step.argtypes = [G, i32, i32, vp, vp, vp, C, vp, vp, i32, i32, f32, vp,
-                                        vp, vp, vp, vp, sz, vp]
+                                        vp, vp, vp, vp, sz, vp, O]
         lib.rkv_decode_step.restype = ctypes.c_int
         if check_build_id:
             built = lib.rkv_build_id().decode()
@@ -184,23 +213,23 @@ class PagedCache:
 
 
 def decode_mode(g: rkv_gqa, B: int, page_size: int, max_pages: int, k2: int, k1: int = 1,
-                dtype: int = RKV_BF16) -> int:
-    """How rkv_decode_step runs for these shapes (rkv_decode_mode: the rule
-    documented in include/rkv.h, RKV_FUSED=0/1/2 overriding it): 0 = the
-    standalone kernels, 1 = one fused kernel with a block per (sequence, KV
-    head), 2 = the fused kernel split K-wise over several blocks per unit,
-    plus the merge."""
-    mode = load_library().rkv_decode_mode(ctypes.byref(g), dtype, B, page_size, max_pages, k1, k2)
+                dtype: int = RKV_BF16, opts: rkv_opts | None = None) -> int:
+    """How rkv_decode_step runs for these shapes and options
+    (rkv_decode_mode, the rule documented in include/rkv.h):
+    RKV_FORM_STANDALONE, RKV_FORM_FUSED (one block per (sequence, KV head))
+    or RKV_FORM_SPLITK (the fused kernel split K-wise, plus the merge)."""
+    mode = load_library().rkv_decode_mode(ctypes.byref(g), dtype, B, page_size, max_pages, k1, k2,
+                                          _opt(opts))
     if mode < 0:
         _check("rkv_decode_mode", mode)
     return mode
 
 
 def fused_path(g: rkv_gqa, B: int, page_size: int, max_pages: int, k2: int, k1: int = 1,
-               dtype: int = RKV_BF16) -> bool:
+               dtype: int = RKV_BF16, opts: rkv_opts | None = None) -> bool:
     """Whether rkv_decode_step runs as the fused kernel with one block per
     (sequence, KV head)."""
-    return decode_mode(g, B, page_size, max_pages, k2, k1, dtype) == 1
+    return decode_mode(g, B, page_size, max_pages, k2, k1, dtype, opts) == RKV_FORM_FUSED
 
 
 # ---- entry points (same names as the C ABI) ---------------------------------
@@ -225,7 +254,7 @@ def rkv_prefill_evict(g: rkv_gqa, prompt_lens, keep, q_win: torch.Tensor, k: tor
                       kept_idx: torch.Tensor | None = None,
                       pooled_scores: torch.Tensor | None = None,
                       seq_lens_out: torch.Tensor | None = None,
-                      ws: torch.Tensor | None = None) -> None:
+                      ws: torch.Tensor | None = None, opts: rkv_opts | None = None) -> None:
     """SnapKV++ eviction.  prompt_lens/keep: host sequences of ints (length B);
     q_win [B, Hq, w, d]; k, v [B, Hkv, L_max, d]."""
     _need(k, "k")
@@ -248,7 +277,7 @@ def rkv_prefill_evict(g: rkv_gqa, prompt_lens, keep, q_win: torch.Tensor, k: tor
         ctypes.byref(g), _dtype_code(k), B, lens, keeps, L_max, int(w), int(pool_kernel),
         float(scale), q_win.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(cs),
         _ptr(summaries), _ptr(kept_idx), stride, _ptr(pooled_scores), _ptr(seq_lens_out),
-        ws.data_ptr(), ws.numel(), _stream()))
+        ws.data_ptr(), ws.numel(), _stream(), _opt(opts)))
 
 
 def rkv_prefill_evict_chunk_workspace_bytes(g: rkv_gqa, B: int, L_max: int, w: int) -> int:
@@ -263,7 +292,8 @@ def rkv_prefill_evict_chunk(g: rkv_gqa, n_cached, chunk_lens, keep, q_win: torch
                             kept_idx: torch.Tensor | None = None,
                             pooled_scores: torch.Tensor | None = None,
                             seq_lens_out: torch.Tensor | None = None,
-                            ws: torch.Tensor | None = None) -> None:
+                            ws: torch.Tensor | None = None,
+                            opts: rkv_opts | None = None) -> None:
     """SnapKV++ eviction over the cached rows followed by a prefill chunk.
     n_cached/chunk_lens/keep: host sequences of ints (length B); q_win
     [B, Hq, w, d] (the chunk's last w queries); k_chunk, v_chunk
@@ -291,13 +321,14 @@ def rkv_prefill_evict_chunk(g: rkv_gqa, n_cached, chunk_lens, keep, q_win: torch
         ctypes.byref(g), _dtype_code(k_chunk), B, nc, cl, keeps, C_max, int(w),
         int(pool_kernel), float(scale), q_win.data_ptr(), k_chunk.data_ptr(),
         v_chunk.data_ptr(), ctypes.byref(cs), _ptr(summaries), _ptr(kept_idx), stride,
-        _ptr(pooled_scores), _ptr(seq_lens_out), ws.data_ptr(), ws.numel(), _stream()))
+        _ptr(pooled_scores), _ptr(seq_lens_out), ws.data_ptr(), ws.numel(), _stream(), _opt(opts)))
 
 
 def rkv_append_summaries(g: rkv_gqa, cache: PagedCache, n_old: torch.Tensor,
                          n_new: torch.Tensor, max_new_rows: int, summaries: torch.Tensor,
                          k_src: torch.Tensor | None = None,
-                         v_src: torch.Tensor | None = None) -> None:
+                         v_src: torch.Tensor | None = None,
+                         opts: rkv_opts | None = None) -> None:
     """Fold rows [n_old, n_new) into the page summaries, first copying them
     from k_src/v_src [B, Hkv, max_new_rows, d] into the cache when given."""
     _need(n_old, "n_old", torch.int32)
@@ -309,25 +340,26 @@ def rkv_append_summaries(g: rkv_gqa, cache: PagedCache, n_old: torch.Tensor,
     _check("rkv_append_summaries", load_library().rkv_append_summaries(
         ctypes.byref(g), _dtype_code(summaries), int(n_old.shape[0]), ctypes.byref(cs),
         n_old.data_ptr(), n_new.data_ptr(), int(max_new_rows), _ptr(k_src), _ptr(v_src),
-        summaries.data_ptr(), _stream()))
+        summaries.data_ptr(), _stream(), _opt(opts)))
 
 
 def rkv_hsa_workspace_bytes(g: rkv_gqa, B: int, page_size: int, max_pages: int, k1: int,
-                            k2: int) -> int:
+                            k2: int, opts: rkv_opts | None = None) -> int:
     return int(load_library().rkv_hsa_workspace_bytes(ctypes.byref(g), B, page_size,
-                                                      max_pages, k1, k2))
+                                                      max_pages, k1, k2, _opt(opts)))
 
 
 def hsa_workspace(g: rkv_gqa, B: int, page_size: int, max_pages: int, k1: int, k2: int,
-                  device) -> torch.Tensor:
-    return torch.zeros(rkv_hsa_workspace_bytes(g, B, page_size, max_pages, k1, k2),
+                  device, opts: rkv_opts | None = None) -> torch.Tensor:
+    return torch.zeros(rkv_hsa_workspace_bytes(g, B, page_size, max_pages, k1, k2, opts),
                        dtype=torch.uint8, device=device)
 
 
 def rkv_hsa_select(g: rkv_gqa, q: torch.Tensor, seq_lens: torch.Tensor, page_size: int,
                    summaries: torch.Tensor, k1: int, k2: int, page_idx: torch.Tensor,
                    ws: torch.Tensor, chan_idx: torch.Tensor | None = None,
-                   page_scores: torch.Tensor | None = None) -> None:
+                   page_scores: torch.Tensor | None = None,
+                   opts: rkv_opts | None = None) -> None:
     _need(q, "q")
     _need(seq_lens, "seq_lens", torch.int32)
     _need(summaries, "summaries", q.dtype)
@@ -339,12 +371,12 @@ def rkv_hsa_select(g: rkv_gqa, q: torch.Tensor, seq_lens: torch.Tensor, page_siz
     _check("rkv_hsa_select", load_library().rkv_hsa_select(
         ctypes.byref(g), _dtype_code(q), int(q.shape[0]), q.data_ptr(), seq_lens.data_ptr(),
         int(page_size), max_pages, summaries.data_ptr(), int(k1), int(k2), _ptr(chan_idx),
-        page_idx.data_ptr(), _ptr(page_scores), ws.data_ptr(), ws.numel(), _stream()))
+        page_idx.data_ptr(), _ptr(page_scores), ws.data_ptr(), ws.numel(), _stream(), _opt(opts)))
 
 
 def rkv_hsa_attend(g: rkv_gqa, q: torch.Tensor, cache: PagedCache, seq_lens: torch.Tensor,
                    page_idx: torch.Tensor, k2: int, scale: float, out: torch.Tensor,
-                   ws: torch.Tensor) -> None:
+                   ws: torch.Tensor, opts: rkv_opts | None = None) -> None:
     _need(q, "q", cache.k_pool.dtype)
     _need(seq_lens, "seq_lens", torch.int32)
     _need(page_idx, "page_idx", torch.int32)
@@ -354,14 +386,15 @@ def rkv_hsa_attend(g: rkv_gqa, q: torch.Tensor, cache: PagedCache, seq_lens: tor
     _check("rkv_hsa_attend", load_library().rkv_hsa_attend(
         ctypes.byref(g), _dtype_code(q), int(q.shape[0]), q.data_ptr(), ctypes.byref(cs),
         seq_lens.data_ptr(), page_idx.data_ptr(), int(k2), float(scale), out.data_ptr(),
-        ws.data_ptr(), ws.numel(), _stream()))
+        ws.data_ptr(), ws.numel(), _stream(), _opt(opts)))
 
 
 def rkv_hsa_decode(g: rkv_gqa, q: torch.Tensor, cache: PagedCache, seq_lens: torch.Tensor,
                    summaries: torch.Tensor, k1: int, k2: int, scale: float, out: torch.Tensor,
                    ws: torch.Tensor, chan_idx: torch.Tensor | None = None,
                    page_idx: torch.Tensor | None = None,
-                   page_scores: torch.Tensor | None = None) -> None:
+                   page_scores: torch.Tensor | None = None,
+                   opts: rkv_opts | None = None) -> None:
     _need(q, "q", cache.k_pool.dtype)
     _need(seq_lens, "seq_lens", torch.int32)
     _need(summaries, "summaries", q.dtype)
@@ -375,7 +408,7 @@ def rkv_hsa_decode(g: rkv_gqa, q: torch.Tensor, cache: PagedCache, seq_lens: tor
         ctypes.byref(g), _dtype_code(q), int(q.shape[0]), q.data_ptr(), ctypes.byref(cs),
         seq_lens.data_ptr(), summaries.data_ptr(), int(k1), int(k2), float(scale),
         out.data_ptr(), _ptr(chan_idx), _ptr(page_idx), _ptr(page_scores), ws.data_ptr(),
-        ws.numel(), _stream()))
+        ws.numel(), _stream(), _opt(opts)))
 
 
 def rkv_decode_step(g: rkv_gqa, q: torch.Tensor, k_new: torch.Tensor | None,
@@ -383,7 +416,8 @@ def rkv_decode_step(g: rkv_gqa, q: torch.Tensor, k_new: torch.Tensor | None,
                     summaries: torch.Tensor, k1: int, k2: int, scale: float, out: torch.Tensor,
                     ws: torch.Tensor, chan_idx: torch.Tensor | None = None,
                     page_idx: torch.Tensor | None = None,
-                    page_scores: torch.Tensor | None = None) -> None:
+                    page_scores: torch.Tensor | None = None,
+                    opts: rkv_opts | None = None) -> None:
     """Append the new token (row seq_lens-1 from k_new/v_new [B, Hkv, d]) and
     run HSA decode, in one call per layer."""
     _need(q, "q", cache.k_pool.dtype)
@@ -401,4 +435,4 @@ def rkv_decode_step(g: rkv_gqa, q: torch.Tensor, k_new: torch.Tensor | None,
         ctypes.byref(g), _dtype_code(q), int(q.shape[0]), q.data_ptr(), _ptr(k_new),
         _ptr(v_new), ctypes.byref(cs), seq_lens.data_ptr(), summaries.data_ptr(), int(k1),
         int(k2), float(scale), out.data_ptr(), _ptr(chan_idx), _ptr(page_idx),
-        _ptr(page_scores), ws.data_ptr(), ws.numel(), _stream()))
+        _ptr(page_scores), ws.data_ptr(), ws.numel(), _stream(), _opt(opts)))

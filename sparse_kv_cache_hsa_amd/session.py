@@ -15,10 +15,18 @@ from .workloads import Workload
 
 
 class Session:
-    def __init__(self, wl: Workload, extra_rows: int, device="cuda", layers: int | None = None):
+    """layers: how many layers to hold (the first ones of the model), or
+    layer_ids: which of the model's layers (their seeded data) the session's
+    layer slots hold."""
+
+    def __init__(self, wl: Workload, extra_rows: int, device="cuda", layers: int | None = None,
+                 layer_ids=None):
         self.wl = wl
         self.dev = torch.device(device)
-        self.n_layers = wl.layers if layers is None else layers
+        if layer_ids is None:
+            layer_ids = range(wl.layers if layers is None else layers)
+        self.layer_ids = [int(x) for x in layer_ids]
+        self.n_layers = len(self.layer_ids)
         self.B, self.Hkv, self.G, self.d = wl.batch, wl.n_kv_heads, wl.group, wl.head_dim
         self.Hq, self.P = wl.n_q_heads, wl.page_size
         self.g = rkv.gqa(self.Hkv, self.G, self.d)
@@ -59,12 +67,13 @@ class Session:
         v = torch.zeros_like(k)
         qw = torch.zeros((self.B, self.Hq, wl.window, self.d), dtype=wl.dtype, device=self.dev) \
             if wl.evicts else None
+        lid = self.layer_ids[layer]
         for b, L in enumerate(self.prompt_lens):
-            kb, vb = wl.prompt_kv(layer, b, L, device=self.dev)
+            kb, vb = wl.prompt_kv(lid, b, L, device=self.dev)
             k[b, :, :L] = kb
             v[b, :, :L] = vb
             if qw is not None:
-                qw[b] = wl.window_q(layer, b, L, device=self.dev)
+                qw[b] = wl.window_q(lid, b, L, device=self.dev)
         return k, v, qw
 
     def evict_workspace(self):
@@ -99,7 +108,8 @@ class Session:
         k = torch.zeros((self.B, self.Hkv, n, self.d), dtype=self.wl.dtype, device=self.dev)
         v = torch.zeros_like(k)
         for b in range(self.B):
-            k[b], v[b] = self.wl.turn_rows(layer, b, turn, self.positions()[b], device=self.dev)
+            k[b], v[b] = self.wl.turn_rows(self.layer_ids[layer], b, turn, self.positions()[b],
+                                           device=self.dev)
         n_old = torch.tensor(self.rows, dtype=torch.int32, device=self.dev)
         n_new = n_old + n
         rkv.rkv_append_summaries(self.g, self.caches[layer], n_old, n_new, n, self.summ[layer],
@@ -120,7 +130,8 @@ class Session:
         for s in range(steps):
             per_layer = []
             for l in range(self.n_layers):
-                k, v, q = self.wl.decode_tokens(l, s, pos0 + s, turn=turn, device=self.dev)
+                k, v, q = self.wl.decode_tokens(self.layer_ids[l], s, pos0 + s, turn=turn,
+                                                device=self.dev)
                 per_layer.append((k, v, q))
             n_old = (rows0 + s).to(self.dev)
             n_new = (rows0 + s + 1).to(self.dev)

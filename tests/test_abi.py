@@ -54,7 +54,7 @@ def _call_decode(lib, g, dtype=0, B=1, P=16, max_pages=8, k1=8, k2=4, scale=0.12
     return lib.load_library().rkv_hsa_decode(
         ctypes.byref(g) if g is not None else None, dtype, B, None if null_q else fake,
         ctypes.byref(cache), fake, fake, k1, k2, scale, None if null_out else fake,
-        None, None, None, fake, ws_bytes, None)
+        None, None, None, fake, ws_bytes, None, None)
 
 
 def test_decode_argument_checks(rkv_lib):
@@ -88,7 +88,7 @@ def test_workspace_sizes(rkv_lib):
     # each a (max, sum, acc[128]) partial per query head in fp32
     assert a >= 8 * 16 * 4 * (128 + 2) * 4
     # the split-K partials fit for every batch, also where the default rule
-    # picks another path (RKV_FUSED can force split-K there)
+    # picks another form (the options can force split-K there)
     for (Hkv, G, d, B, k2) in [(8, 4, 128, 24, 64), (8, 4, 128, 32, 64), (8, 4, 128, 1, 32),
                                (2, 4, 64, 1, 16), (1, 4, 128, 200, 1024), (3, 1, 64, 4, 7)]:
         units = B * Hkv
@@ -97,6 +97,16 @@ def test_workspace_sizes(rkv_lib):
         nsp = -(-k2 // pps)
         need = units * nsp * G * (d + 2) * 4
         assert L.rkv_hsa_workspace_bytes(L.gqa(Hkv, G, d), B, 16, 400, 32, k2) >= need
+    # the workspace follows the options only, never the environment: the
+    # same arguments give the same size; a larger split-K target needs more
+    os.environ["RKV_FUSED"] = "0"
+    os.environ["RKV_SPLITK_BLOCKS"] = "4096"
+    try:
+        assert L.rkv_hsa_workspace_bytes(g, 1, 16, 256, 32, 32) == a
+    finally:
+        del os.environ["RKV_FUSED"], os.environ["RKV_SPLITK_BLOCKS"]
+    big = L.rkv_hsa_workspace_bytes(g, 1, 16, 256, 32, 32, L.make_opts(splitk_blocks=256))
+    assert big >= a + 8 * 16 * 4 * (128 + 2) * 4
     e1 = L.rkv_prefill_evict_workspace_bytes(g, 1, 32768, 32)
     # logits for 128 window rows over 32K keys dominate: 4 B each
     assert e1 >= 8 * 32768 * 128 * 4
@@ -115,7 +125,7 @@ def test_evict_argument_checks(rkv_lib):
         return lib.rkv_prefill_evict(
             ctypes.byref(g), 0, B, (ctypes.c_int32 * B)(*lens), (ctypes.c_int32 * B)(*keeps),
             L_max, w, pool, 0.125, fake, fake, fake, ctypes.byref(cache), None,
-            fake if stride else None, stride, None, None, fake, ws, None)
+            fake if stride else None, stride, None, None, fake, ws, None, None)
 
     assert call([50], [20], pool=4) == L.RKV_EINVAL          # even pooling kernel
     assert call([50], [5]) == L.RKV_EINVAL                   # keep below window
@@ -138,7 +148,7 @@ def test_evict_chunk_argument_checks(rkv_lib):
         arr = lambda xs: (ctypes.c_int32 * B)(*xs)
         return lib.rkv_prefill_evict_chunk(
             ctypes.byref(g), 0, B, arr(n_cached), arr(chunks), arr(keeps), C_max, w, 7, 0.125,
-            fake, fake, fake, ctypes.byref(cache), None, None, 0, None, None, fake, ws, None)
+            fake, fake, fake, ctypes.byref(cache), None, None, 0, None, None, fake, ws, None, None)
 
     assert call([40], [30], [20], w=40) == L.RKV_EINVAL     # evicting with a chunk below w
     assert call([40], [120], [20]) == L.RKV_EINVAL          # chunk longer than C_max
@@ -148,27 +158,41 @@ def test_evict_chunk_argument_checks(rkv_lib):
     assert lib.rkv_prefill_evict_chunk_workspace_bytes(ctypes.byref(g), 1, 70, 8) > 0
 
 
-def test_decode_mode_rule(rkv_lib, monkeypatch):
-    """Which decode form runs (host-only query): the documented rule and the
-    RKV_FUSED overrides, and argument errors."""
+def test_decode_mode_rule(rkv_lib):
+    """Which decode form runs (host-only query): the documented rule, forms
+    forced through rkv_opts, and argument errors.  The environment plays no
+    part."""
     L = rkv_lib
-    monkeypatch.delenv("RKV_FUSED", raising=False)
+    S, F, K = L.RKV_FORM_STANDALONE, L.RKV_FORM_FUSED, L.RKV_FORM_SPLITK
     g = L.gqa(8, 4, 128)
-    assert L.decode_mode(g, 32, 16, 400, 64, 32) == 1      # 256 units fill the chip
-    assert L.decode_mode(g, 1, 16, 216, 32, 32) == 2       # batch 1: split-K
-    assert L.decode_mode(g, 4, 32, 4400, 128, 32) == 0     # beyond the fused page limit
-    assert L.decode_mode(g, 1, 16, 600, 32, 32) == 0       # stage too small for 600 pages
-    assert L.decode_mode(L.gqa(2, 8, 128), 1, 16, 64, 16, 16) == 0   # G > 4
-    assert L.decode_mode(L.gqa(2, 4, 64), 1, 16, 130, 16, 16, L.RKV_F32) == 2
-    monkeypatch.setenv("RKV_FUSED", "0")
-    assert L.decode_mode(g, 32, 16, 400, 64, 32) == 0
-    monkeypatch.setenv("RKV_FUSED", "2")
-    assert L.decode_mode(g, 32, 16, 400, 64, 32) == 2
-    assert L.decode_mode(g, 1, 16, 600, 32, 32) == 0       # cannot be forced past the stage
-    monkeypatch.setenv("RKV_FUSED", "1")
-    assert L.decode_mode(g, 1, 16, 216, 32, 32) == 1
+    os.environ["RKV_FUSED"] = "0"
+    try:
+        assert L.decode_mode(g, 32, 16, 400, 64, 32) == F      # 256 units fill the chip
+    finally:
+        del os.environ["RKV_FUSED"]
+    assert L.decode_mode(g, 1, 16, 216, 32, 32) == K       # batch 1: split-K
+    assert L.decode_mode(g, 4, 32, 4400, 128, 32) == S     # beyond the fused page limit
+    assert L.decode_mode(g, 1, 16, 600, 32, 32) == S       # stage too small for 600 pages
+    assert L.decode_mode(L.gqa(2, 8, 128), 1, 16, 64, 16, 16) == S   # G > 4
+    assert L.decode_mode(L.gqa(2, 4, 64), 1, 16, 130, 16, 16, L.RKV_F32) == K
+    o = L.make_opts
+    assert L.decode_mode(g, 32, 16, 400, 64, 32, opts=o(form=S)) == S
+    assert L.decode_mode(g, 32, 16, 400, 64, 32, opts=o(form=K)) == K
+    assert L.decode_mode(g, 1, 16, 600, 32, 32, opts=o(form=K)) == S   # not past the stage
+    assert L.decode_mode(g, 1, 16, 216, 32, 32, opts=o(form=F)) == F
+    assert L.decode_mode(g, 4, 32, 4400, 128, 32, opts=o(form=F)) == S  # not past the limits
+    assert L.decode_mode(g, 1, 16, 216, 32, 32, opts=o(form=L.RKV_FORM_AUTO)) == K
     lib = L.load_library()
-    assert lib.rkv_decode_mode(ctypes.byref(g), 1, 0, 16, 100, 8, 8) == L.RKV_EINVAL
-    assert lib.rkv_decode_mode(ctypes.byref(g), 1, 1, 16, 100, 0, 8) == L.RKV_EINVAL
-    assert lib.rkv_decode_mode(ctypes.byref(g), 7, 1, 16, 100, 8, 8) == L.RKV_EUNSUPPORTED
-    assert lib.rkv_decode_mode(None, 1, 1, 16, 100, 8, 8) == L.RKV_EINVAL
+    assert lib.rkv_decode_mode(ctypes.byref(g), 1, 0, 16, 100, 8, 8, None) == L.RKV_EINVAL
+    assert lib.rkv_decode_mode(ctypes.byref(g), 1, 1, 16, 100, 0, 8, None) == L.RKV_EINVAL
+    assert lib.rkv_decode_mode(ctypes.byref(g), 7, 1, 16, 100, 8, 8, None) == L.RKV_EUNSUPPORTED
+    assert lib.rkv_decode_mode(None, 1, 1, 16, 100, 8, 8, None) == L.RKV_EINVAL
+
+
+def test_no_environment_lookups_in_the_library():
+    """Every choice the library makes comes from its arguments: no source
+    file reads the environment."""
+    csrc = os.path.join(ROOT, "sparse_kv_cache_hsa_amd", "csrc")
+    for name in os.listdir(csrc):
+        text = open(os.path.join(csrc, name)).read()
+        assert "getenv" not in text and "environ" not in text, name

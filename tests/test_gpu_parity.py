@@ -45,9 +45,11 @@ DECODE_CASES = [
 ]
 
 
-def run_decode_case(case, seed, q_override=None, k_override=None, mode="decode"):
+def run_decode_case(case, seed, q_override=None, k_override=None, mode="decode", opts=None):
     """mode: "decode" (rkv_hsa_decode on a filled cache) or "step" (the cache
-    holds rows [0, n-1) and rkv_decode_step appends row n-1 itself)."""
+    holds rows [0, n-1) and rkv_decode_step appends row n-1 itself).  opts:
+    execution options (rkv_opts) passed to the decode call and used to size
+    its workspace."""
     rkv = lib()
     dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages = case
     Lmax = max(max(lens), 1)
@@ -70,14 +72,14 @@ def run_decode_case(case, seed, q_override=None, k_override=None, mode="decode")
     chan = torch.full((B, Hkv, k1), -7, dtype=torch.int32, device="cuda")
     pidx = torch.full((B, Hkv, k2), -7, dtype=torch.int32, device="cuda")
     scores = torch.zeros((B, Hkv, max_pages), dtype=torch.float32, device="cuda")
-    ws = rkv.hsa_workspace(g, B, P, max_pages, k1, k2, "cuda")
+    ws = rkv.hsa_workspace(g, B, P, max_pages, k1, k2, "cuda", opts)
     scale = scale_for(d)
     if mode == "step":
         rkv.rkv_decode_step(g, qd, k_new, v_new, cache, seq, summ, k1, k2, scale, out, ws,
-                            chan_idx=chan, page_idx=pidx, page_scores=scores)
+                            chan_idx=chan, page_idx=pidx, page_scores=scores, opts=opts)
     else:
         rkv.rkv_hsa_decode(g, qd, cache, seq, summ, k1, k2, scale, out, ws, chan_idx=chan,
-                           page_idx=pidx, page_scores=scores)
+                           page_idx=pidx, page_scores=scores, opts=opts)
     torch.cuda.synchronize()
     if mode == "step":
         # the appended row sits in the pool at its page's block
@@ -112,28 +114,36 @@ def run_decode_case(case, seed, q_override=None, k_override=None, mode="decode")
     return worst, out
 
 
-@pytest.fixture(params=["auto", "fused", "splitk", "split", "split-legacy"])
-def path(request, monkeypatch):
-    """Which implementation rkv_hsa_decode / rkv_decode_step dispatch to:
-    the default rule, the fused kernel with one block per unit, the fused
-    kernel split K-wise (plus the merge), or the standalone kernels (with
-    several selection chunks: rank-ordered candidates and the rank-search
-    merge by default, "split-legacy" the radix top-k and radix merge)."""
-    env = {"fused": "1", "splitk": "2", "split": "0", "split-legacy": "0"}.get(request.param)
-    if env is not None:
-        monkeypatch.setenv("RKV_FUSED", env)
-    if request.param == "split-legacy":
-        monkeypatch.setenv("RKV_SELECT_SORTED", "0")
+PATH_OPTS = {
+    "auto": {},
+    "fused": {"form": 2},
+    "splitk": {"form": 3},
+    "split": {"form": 1},
+    "split-legacy": {"form": 1, "select_radix": 1},
+}
+
+
+def path_opts(name):
+    return lib().make_opts(**PATH_OPTS[name])
+
+
+@pytest.fixture(params=list(PATH_OPTS))
+def path(request):
+    """Which implementation rkv_hsa_decode / rkv_decode_step dispatch to,
+    as explicit rkv_opts: the default rule, the fused kernel with one block
+    per unit, the fused kernel split K-wise (plus the merge), or the
+    standalone kernels (with several selection chunks: rank-ordered
+    candidates and the rank-search merge by default, "split-legacy" the
+    radix top-k and radix merge)."""
     return request.param
 
 
-def case_mode(case):
-    """The decode mode the library picks for a case under the current
-    RKV_FUSED setting."""
+def case_mode(case, opts=None):
+    """The decode form the library picks for a case and options."""
     dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages = case
     rkv = lib()
     return rkv.decode_mode(rkv.gqa(Hkv, G, d), B, P, max_pages, k2, k1,
-                           rkv.RKV_F32 if dtype == F32 else rkv.RKV_BF16)
+                           rkv.RKV_F32 if dtype == F32 else rkv.RKV_BF16, opts)
 
 
 def fused_supported(case):
@@ -145,25 +155,26 @@ def fused_supported(case):
 @pytest.mark.parametrize("mode", ["decode", "step"])
 def test_decode_matches_oracle(ci, mode, path):
     case = DECODE_CASES[ci]
+    opts = path_opts(path)
     if path == "fused" and not fused_supported(case):
         pytest.skip("shape outside the fused kernel's limits (dispatches to the split path)")
-    if path == "splitk" and case_mode(case) != 2:
+    if path == "splitk" and case_mode(case, opts) != 3:
         pytest.skip("shape outside the split-K fused kernel's limits")
-    run_decode_case(case, 1000 + ci, mode=mode)
+    run_decode_case(case, 1000 + ci, mode=mode, opts=opts)
 
 
 # A batch large enough for the fused kernel by default (B * Hkv >= 192).
 BIG_CASE = (BF16, 24, 8, 4, 128, 16, 32, 64, [4000 + 37 * i for i in range(24)], 320)
 
 
-def test_splitk_appended_row_read_by_a_later_split(monkeypatch):
+def test_splitk_appended_row_read_by_a_later_split():
     """Split-K fused path, one page per split: the appended row's key points
     along the group's queries, so its page (the highest selected index) is
     attended by the last split, not by the block that stores the row.  The
     output must match the oracle, and the pool must hold the new row."""
-    monkeypatch.setenv("RKV_FUSED", "2")
+    opts = path_opts("splitk")
     case = (BF16, 2, 2, 4, 128, 16, 32, 16, [1000, 777], 80)
-    assert case_mode(case) == 2
+    assert case_mode(case, opts) == 3
     dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages = case
     K = rand((B, Hkv, max(lens), d), 4100, dtype, 1.5)
     q = rand((B, Hkv * G, d), 4102, dtype)
@@ -171,19 +182,19 @@ def test_splitk_appended_row_read_by_a_later_split(monkeypatch):
         for h in range(Hkv):
             qs = q[b, h * G:(h + 1) * G].float().sum(0)
             K[b, h, lens[b] - 1] = (8.0 * qs / qs.norm()).to(dtype)
-    run_decode_case(case, 4100, q_override=q, k_override=K, mode="step")
+    run_decode_case(case, 4100, q_override=q, k_override=K, mode="step", opts=opts)
 
 
 def test_decode_large_batch_default_path():
     run_decode_case(BIG_CASE, 77, mode="step")
 
 
-def test_fused_and_split_select_identically(monkeypatch):
+def test_fused_and_split_select_identically():
     outs = []
-    for env in ("1", "2", "0"):
-        monkeypatch.setenv("RKV_FUSED", env)
-        assert case_mode(BIG_CASE) == int(env)
-        outs.append(run_decode_case(BIG_CASE, 78, mode="step")[1].clone())
+    for name, form in (("fused", 2), ("splitk", 3), ("split", 1)):
+        opts = path_opts(name)
+        assert case_mode(BIG_CASE, opts) == form
+        outs.append(run_decode_case(BIG_CASE, 78, mode="step", opts=opts)[1].clone())
     for o in outs[1:]:
         assert (outs[0] - o).abs().max().item() < 1e-5
 
@@ -247,11 +258,11 @@ def test_append_in_chunks_matches_rebuild(dtype):
                        summ2.view(torch.int16 if dtype == BF16 else torch.int32))
 
 
-@pytest.mark.parametrize("fused", ["1", "2", "0"])
-def test_tiny_workload_decode_loop(fused, monkeypatch):
+@pytest.mark.parametrize("form", ["fused", "splitk", "split"])
+def test_tiny_workload_decode_loop(form):
     """The tiny fp32 workload end to end: 2,048 cached rows, 32 decode steps,
     each appending its token and decoding in one rkv_decode_step call."""
-    monkeypatch.setenv("RKV_FUSED", fused)
+    opts = path_opts(form)
     rkv = lib()
     wl = workloads.TINY
     B, Hkv, G, d, P = wl.batch, wl.n_kv_heads, wl.group, wl.head_dim, wl.page_size
@@ -271,7 +282,7 @@ def test_tiny_workload_decode_loop(fused, monkeypatch):
     for h in range(Hkv):
         Ko[h][:n0], Vo[h][:n0] = k0[h].numpy(), v0[h].numpy()
         oracle.summaries_append(Ko[h], 0, n0, P, smax[h], smin[h])
-    ws = rkv.hsa_workspace(g, B, P, max_pages, wl.k1, wl.k2, "cuda")
+    ws = rkv.hsa_workspace(g, B, P, max_pages, wl.k1, wl.k2, "cuda", opts)
     out = torch.zeros((B, Hkv * G, d), device="cuda")
     pidx = torch.zeros((B, Hkv, wl.k2), dtype=torch.int32, device="cuda")
     chan = torch.zeros((B, Hkv, wl.k1), dtype=torch.int32, device="cuda")
@@ -281,7 +292,7 @@ def test_tiny_workload_decode_loop(fused, monkeypatch):
         kt, vt, qt = wl.decode_tokens(0, step, torch.tensor([n]))
         seq = torch.tensor([n + 1], dtype=torch.int32, device="cuda")
         rkv.rkv_decode_step(g, qt.cuda(), kt.cuda(), vt.cuda(), cache, seq, summ, wl.k1, wl.k2,
-                            scale, out, ws, chan_idx=chan, page_idx=pidx)
+                            scale, out, ws, chan_idx=chan, page_idx=pidx, opts=opts)
         torch.cuda.synchronize()
         for h in range(Hkv):
             Ko[h][n], Vo[h][n] = kt[0, h].numpy(), vt[0, h].numpy()
@@ -367,11 +378,12 @@ PARAM_CASES = {
 @pytest.mark.parametrize("mode", ["decode", "step"])
 def test_selection_parameterisations(name, mode, path):
     case = PARAM_CASES[name]
+    opts = path_opts(path)
     if path == "fused" and not fused_supported(case):
         pytest.skip("shape outside the fused kernel's limits")
-    if path == "splitk" and case_mode(case) != 2:
+    if path == "splitk" and case_mode(case, opts) != 3:
         pytest.skip("shape outside the split-K fused kernel's limits")
-    run_decode_case(case, 3000 + len(name), mode=mode)
+    run_decode_case(case, 3000 + len(name), mode=mode, opts=opts)
 
 
 def test_exact_topk_is_the_top_of_the_true_scores():
@@ -439,11 +451,12 @@ RANDOM_CASES = _random_cases(16, 2024)
 @pytest.mark.parametrize("mode", ["decode", "step"])
 def test_random_shapes_match_oracle(ci, mode, path):
     case = RANDOM_CASES[ci]
+    opts = path_opts(path)
     if path == "fused" and not fused_supported(case):
         pytest.skip("shape outside the fused kernel's limits")
-    if path == "splitk" and case_mode(case) != 2:
+    if path == "splitk" and case_mode(case, opts) != 3:
         pytest.skip("shape outside the split-K fused kernel's limits")
-    run_decode_case(case, 5000 + ci, mode=mode)
+    run_decode_case(case, 5000 + ci, mode=mode, opts=opts)
 
 
 @pytest.mark.parametrize("dtype", [F32, BF16])
@@ -515,3 +528,83 @@ def test_prefill_evict_chunked_matches_oracle(dtype):
         offsets = [offsets[b] + cl[b] for b in range(B)]
     print(f"chunked eviction near-tie swaps: {swaps}")
     assert sum(live.values()) >= len(live) - 1
+
+
+@pytest.mark.parametrize("form", ["fused", "splitk", "split"])
+def test_device_status_word(form):
+    """Device-side inputs the kernels must clamp or skip are reported in the
+    optional status word (rkv_opts.status): a row count beyond the cache's
+    capacity (RKV_DEV_LENGTH), a page-table entry outside the pool
+    (RKV_DEV_BLOCK) and, for rkv_hsa_attend, a page index outside the
+    sequence (RKV_DEV_PAGE).  Clean calls leave the word at zero, and the
+    sequences with valid inputs still match the oracle."""
+    rkv = lib()
+    dtype, B, Hkv, G, d, P, k1, k2, max_pages = BF16, 2, 2, 4, 128, 16, 32, 4, 8
+    lens = [100, 50]
+    K = rand((B, Hkv, 128, d), 61, dtype, 1.5)
+    V = rand((B, Hkv, 128, d), 62, dtype)
+    q = rand((B, Hkv * G, d), 63, dtype)
+    g = rkv.gqa(Hkv, G, d)
+    cache, summ = make_cache(Hkv, d, P, max_pages, [max_pages] * B, dtype, 64)
+    fill_cache(g, cache, summ, K.cuda(), V.cuda(), lens)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    opts = lib().make_opts(**PATH_OPTS[form], status=status)
+    ws = rkv.hsa_workspace(g, B, P, max_pages, k1, k2, "cuda", opts)
+    out = torch.zeros((B, Hkv * G, d), device="cuda")
+    pidx = torch.zeros((B, Hkv, k2), dtype=torch.int32, device="cuda")
+    scale = scale_for(d)
+    qd = q.cuda()
+
+    def decode(seq_lens):
+        status.zero_()
+        rkv.rkv_hsa_decode(g, qd, cache, torch.tensor(seq_lens, dtype=torch.int32, device="cuda"),
+                           summ, k1, k2, scale, out, ws, page_idx=pidx, opts=opts)
+        torch.cuda.synchronize()
+        return int(status.item())
+
+    def check_seq(b):
+        n = lens[b]
+        for h in range(Hkv):
+            smax, smin = oracle.summaries_rebuild(bits(K[b, h, :n]), P)
+            _, p_o, _, out_o = oracle.hsa_group(bits(q[b, h * G:(h + 1) * G]), bits(K[b, h, :n]),
+                                                bits(V[b, h, :n]), smax, smin, n, P, k1, k2, scale)
+            np.testing.assert_array_equal(pidx[b, h].cpu().numpy(), p_o)
+            assert max_abs_err(out[b, h * G:(h + 1) * G], out_o) <= OUT_ATOL
+
+    assert decode(lens) == 0
+    check_seq(0)
+    check_seq(1)
+    # sequence 0 claims more rows than max_pages * P = 128
+    assert decode([200, 50]) == rkv.RKV_DEV_LENGTH
+    check_seq(1)
+    assert decode([-3, 50]) == rkv.RKV_DEV_LENGTH
+    check_seq(1)
+    # a page of sequence 0 points outside the pool; k2 = 4 of its 7 pages
+    # with one of them broken must touch it for some head or not at all, so
+    # every page is made selectable by asking for all of them
+    saved = cache.page_table.clone()
+    cache.page_table[0, 2] = cache.k_pool.shape[0] + 5
+    status.zero_()
+    k2_all = 8
+    ws_all = rkv.hsa_workspace(g, B, P, max_pages, k1, k2_all, "cuda", opts)
+    pidx_all = torch.zeros((B, Hkv, k2_all), dtype=torch.int32, device="cuda")
+    rkv.rkv_hsa_decode(g, qd, cache, torch.tensor(lens, dtype=torch.int32, device="cuda"), summ,
+                       k1, k2_all, scale, out, ws_all, page_idx=pidx_all, opts=opts)
+    torch.cuda.synchronize()
+    assert int(status.item()) == rkv.RKV_DEV_BLOCK
+    cache.page_table.copy_(saved)
+    # rkv_hsa_attend with a page index outside sequence 1's 4 pages
+    bad = pidx.clone()
+    bad[1, 0, 0] = 6
+    status.zero_()
+    rkv.rkv_hsa_attend(g, qd, cache, torch.tensor(lens, dtype=torch.int32, device="cuda"), bad,
+                       k2, scale, out, ws, opts=opts)
+    torch.cuda.synchronize()
+    assert int(status.item()) == rkv.RKV_DEV_PAGE
+    # an append whose row counts exceed the capacity
+    status.zero_()
+    rkv.rkv_append_summaries(g, cache, torch.tensor([100, 50], dtype=torch.int32, device="cuda"),
+                             torch.tensor([300, 50], dtype=torch.int32, device="cuda"), 8,
+                             torch.zeros_like(summ), opts=opts)
+    torch.cuda.synchronize()
+    assert int(status.item()) == rkv.RKV_DEV_LENGTH
