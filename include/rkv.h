@@ -128,7 +128,18 @@ typedef struct rkv_opts {
                                (0 = automatic) */
     int32_t *status;        /* device int32, optional: RKV_DEV_* flags are ORed in; the
                                library never clears it */
+    uint64_t *trace;        /* device buffer, optional, read only by a library built with
+                               RKV_PHASE_TIMING: the fused decode kernel writes
+                               RKV_TRACE_SLOTS clock stamps per block (block x + gridDim.x *
+                               (y + gridDim.y * z)); ignored by the normal build */
 } rkv_opts;
+
+/* Phase stamps of the fused decode kernel in a RKV_PHASE_TIMING build, in
+ * units of the device's constant wall clock (hipDeviceAttributeWallClockRate):
+ * slot 0 block start, 1 queries loaded, 2 channels ranked, 3 summaries
+ * staged, 4 pages chosen, 5 row table built (stream starts), 6..21 the end of
+ * each of the 16 waves' streams, 22 block end, 23 the XCC the block ran on. */
+#define RKV_TRACE_SLOTS 24
 
 /* Human-readable text for a status code (static storage). */
 const char *rkv_status_string(int status);

@@ -18,6 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "librkv.so")
+LIB_TIMING_PATH = os.path.join(PKG, "librkv_timing.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -51,14 +52,20 @@ def _hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip and link librkv.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, timing: bool = False) -> str:
+    """Compile every csrc/*.hip and link librkv.so; returns its path.
+    timing=True builds librkv_timing.so instead: the same sources with
+    RKV_PHASE_TIMING defined (the fused decode kernel writes per-phase clock
+    stamps into rkv_opts.trace), for the phase table only."""
+    build_dir = BUILD_DIR + ("_timing" if timing else "")
+    os.makedirs(build_dir, exist_ok=True)
     bid = source_hash()
     hipcc = _hipcc()
     flags = HIPCC_FLAGS + [f"-I{INCLUDE}", f"-I{CSRC}", f'-DRKV_BUILD_ID="{bid}"']
+    if timing:
+        flags.append("-DRKV_PHASE_TIMING")
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in srcs]
+    objs = [os.path.join(build_dir, os.path.basename(s) + ".o") for s in srcs]
 
     def compile_one(pair):
         src, obj = pair
@@ -75,16 +82,18 @@ def build(verbose: bool = False) -> str:
         for warn in ex.map(compile_one, zip(srcs, objs)):
             if verbose and warn:
                 print(warn)
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
+    lib_path = LIB_TIMING_PATH if timing else LIB_PATH
+    tmp = lib_path + f".tmp{os.getpid()}"
     # --no-undefined: a kernel whose host-side launch stub was not emitted
     # fails here instead of at load time
     cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,--no-undefined", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, timing="--timing" in sys.argv))

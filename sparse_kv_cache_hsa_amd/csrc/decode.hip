@@ -50,7 +50,23 @@ struct DecArgs {
     float *part;  // split-K: [B][Hkv][n_splits][G][D + 2] partials
     int pps;      // split-K: selected pages per split
     int32_t *status;
+    uint64_t *trace;  // RKV_PHASE_TIMING builds: RKV_TRACE_SLOTS stamps per block
 };
+
+// Phase stamps (RKV_PHASE_TIMING builds only): thread 0 of the block, or lane
+// 0 of a wave, writes the constant-rate wall clock into its slot.
+#ifdef RKV_PHASE_TIMING
+#define RKV_STAMP(cond, slot)                                                          \
+    do {                                                                               \
+        if (a.trace && (cond))                                                         \
+            a.trace[(((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x +     \
+                     blockIdx.x) * RKV_TRACE_SLOTS + (slot)] = wall_clock64();         \
+    } while (0)
+#else
+#define RKV_STAMP(cond, slot) \
+    do {                      \
+    } while (0)
+#endif
 
 template <typename T, int D, int G, bool SPLIT>
 __global__ void __launch_bounds__(kBlock)
@@ -113,8 +129,10 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         vx = v_new[bh * D + tid];
         xs[tid] = x;
     }
+    RKV_STAMP(tid == 0, 0);
     load_group_q<T, D, G, kBlock>(q, bh, qs);
     lds_barrier();
+    RKV_STAMP(tid == 0, 1);
 
     // 2. channels.  The page-table row and the appended page's old summary
     //    (which depend on the row count) are loaded into registers
@@ -130,6 +148,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     }
     rank_channels<D, G, kBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot,
                                 kPacked ? qpm_s : nullptr);
+    RKV_STAMP(tid == 0, 2);
     if (a.chan_out && lead && tid < k1) a.chan_out[bh * k1 + tid] = ch_s[tid];
 
     // 3. the appended row is folded into its page's summary (first of equal
@@ -177,6 +196,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             stage[(int64_t)(k1 + tid) * npad + p_new] = ovr_lo[c];
         }
         lds_barrier();
+        RKV_STAMP(tid == 0, 3);
         uint64_t key = 0;
         if (tid < NP) {
             float sc;
@@ -222,6 +242,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         topk_ascending<kBlock>(comp_s, NP, K, cnt_s, hist, sh, wave_tot, emit);
     }
     lds_barrier();
+    RKV_STAMP(tid == 0, 4);
 
     // 5. resolve the rows of the selected pages, then stream them.  The full
     //    barrier makes the appended K/V row (a global store of this block)
@@ -260,7 +281,9 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     Core core;
     core.init_lds(qs, a.qscale);
     __syncthreads();
+    RKV_STAMP(tid == 0, 5);
     core.stream(row_s, nrows, k_pool, v_pool);
+    RKV_STAMP((tid & (kWave - 1)) == 0, 6 + tid / kWave);
     core.to_shared(csh);
     lds_barrier();
     if constexpr (SPLIT) {
@@ -282,6 +305,15 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     // barrier before the stream (which waits for this wave's stores)
     if (a.page_out && lead)
         for (int o = tid; o < k2; o += kBlock) a.page_out[bh * k2 + o] = o < K ? sel_s[o] : -1;
+#ifdef RKV_PHASE_TIMING
+    lds_barrier();
+    RKV_STAMP(tid == 0, 22);
+    // XCC_ID hardware register (id 20), bits [3:0]
+    if (a.trace && tid == 0)
+        a.trace[(((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) *
+                    RKV_TRACE_SLOTS + 23] =
+            (uint64_t)(__builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 15);
+#endif
 }
 
 template <typename T, int D, int G>
@@ -356,7 +388,7 @@ int launch_decode_fused(const FusedPlan &pl, const rkv_gqa &g, int dtype, int B,
                         const void *k_new, const void *v_new, const rkv_paged_cache &c,
                         const int32_t *seq_lens, void *summaries, int k1, int k2, float scale,
                         float *out, int32_t *chan_idx, int32_t *page_idx, float *page_scores,
-                        float *part, size_t part_bytes, int32_t *status, hipStream_t s) {
+                        float *part, size_t part_bytes, const Knobs &kn, hipStream_t s) {
     DecArgs a;
     a.Hkv = g.n_kv_heads;
     a.P = c.page_size;
@@ -373,7 +405,8 @@ int launch_decode_fused(const FusedPlan &pl, const rkv_gqa &g, int dtype, int B,
     a.score_out = page_scores;
     a.part = part;
     a.pps = pl.pages_per_split;
-    a.status = status;
+    a.status = kn.status;
+    a.trace = kn.trace;
     const int nsp = pl.form == RKV_FORM_SPLITK ? pl.n_splits : 0;
     if (nsp > 0 && (!part || (size_t)B * g.n_kv_heads * nsp * g.group * (g.head_dim + 2) *
                                      sizeof(float) > part_bytes))

@@ -303,7 +303,7 @@ int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
         const size_t off = w.select + w.attend + w.pages;
         return launch_decode_fused(fp, *g, dtype, B, q, k_new, v_new, *cache, seq_lens, summaries,
                                    k1, k2, scale, out, chan_idx, page_idx, page_scores,
-                                   (float *)(base + off), ws_bytes - off, kn.status, s);
+                                   (float *)(base + off), ws_bytes - off, kn, s);
     }
     if (!page_idx) page_idx = (int32_t *)(base + w.select + w.attend);
     // the select kernel appends the new token itself

@@ -324,6 +324,7 @@ struct Knobs {
     int attend_variant = 0;
     int attend_pages = 0;
     int32_t *status = nullptr;
+    uint64_t *trace = nullptr;
 };
 inline Knobs knobs_of(const rkv_opts *o) {
     Knobs k;
@@ -335,6 +336,7 @@ inline Knobs knobs_of(const rkv_opts *o) {
         k.attend_variant = o->attend_variant;
         k.attend_pages = o->attend_pages;
         k.status = o->status;
+        k.trace = o->trace;
     }
     return k;
 }
@@ -395,7 +397,7 @@ int launch_decode_fused(const FusedPlan &pl, const rkv_gqa &g, int dtype, int B,
                         const void *k_new, const void *v_new, const rkv_paged_cache &c,
                         const int32_t *seq_lens, void *summaries, int k1, int k2, float scale,
                         float *out, int32_t *chan_idx, int32_t *page_idx, float *page_scores,
-                        float *part, size_t part_bytes, int32_t *status, hipStream_t s);
+                        float *part, size_t part_bytes, const Knobs &kn, hipStream_t s);
 
 struct EvictSeq {
     int32_t L[RKV_MAX_EVICT_BATCH];

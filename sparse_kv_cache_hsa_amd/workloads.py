@@ -146,11 +146,15 @@ class Workload:
                                 positions=self._pos(start, n, device))
         v = synth.gaussian_rows(self.seed, (self.name, "turn_v", layer, seq, turn),
                                 self.n_kv_heads, n, self.head_dim, device=device, outliers=o)
+        at = self.turn_needle_offset(layer, seq, turn)
+        self._plant(k, layer, list(range(at, at + max(1, self.needle_span))), turn)
+        return k.to(self.dtype), v.to(self.dtype)
+
+    def turn_needle_offset(self, layer: int, seq: int, turn: int) -> int:
+        """Row offset, within a turn's appended rows, of that turn's needle."""
         g = synth.generator(self.seed, self.name, "turn_needle", layer, seq, turn)
         span = max(1, self.needle_span)
-        at = int(torch.randint(0, max(1, n - span), (1,), generator=g))
-        self._plant(k, layer, list(range(at, at + span)), turn)
-        return k.to(self.dtype), v.to(self.dtype)
+        return int(torch.randint(0, max(1, self.turn_append - span), (1,), generator=g))
 
     def decode_tokens(self, layer: int, step: int, positions: torch.Tensor, turn: int = 0,
                       device="cpu"):
