@@ -85,7 +85,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     __shared__ int32_t sel_s[RKV_MAX_K2];
     __shared__ int32_t blk_s[kFusedMaxPages];
     __shared__ int cnt_s[kBlock];
-    __shared__ uint64_t sort_s[kBlock];  // page keys of the staged path's top-k
+    __shared__ uint32_t pkey_s[kBlock];  // page score keys of the staged path's top-k
     __shared__ uint32_t hist[256];
     __shared__ int wave_tot[kNW];
     __shared__ int sh[2];
@@ -146,8 +146,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             omin = sm_min[im];
         }
     }
-    rank_channels<D, G, kBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot,
-                                kPacked ? qpm_s : nullptr);
+    rank_channels_wave<D, G>(qs, k1, ch_s, qsel, kPacked ? qpm_s : nullptr);
     RKV_STAMP(tid == 0, 2);
     if (a.chan_out && lead && tid < k1) a.chan_out[bh * k1 + tid] = ch_s[tid];
 
@@ -197,26 +196,22 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         }
         lds_barrier();
         RKV_STAMP(tid == 0, 3);
-        uint64_t key = 0;
+        // every page's score key to LDS (0 past the last page: below every
+        // real key), then the first wave picks the top K in page order
+        uint32_t skey = 0u;
         if (tid < NP) {
             float sc;
             if constexpr (kPacked)
                 sc = staged_bound_exact<G>((const uint16_t *)stage, npad, tid, k1, qpm_s);
             else
                 sc = staged_bound<T, D, G>(stage, npad, tid, k1, qsel);
-            key = composite_key(ordered_key(sc), tid);
+            skey = ordered_key(sc);
             if (a.score_out && lead) a.score_out[bh * max_pages + tid] = sc;
         }
-        // the sorted keys have LDS of their own, so no barrier is needed
-        // between scoring and sorting
-        if (K > 0) {
-            if (K <= kWave)
-                topk_small<kBlock>(key, NP, K, sort_s, emit);
-            else
-                sort_topk<kBlock>(key, NP, K, sort_s, wave_tot, emit);
-        } else {
-            lds_barrier();
-        }
+        pkey_s[tid] = skey;
+        lds_barrier();
+        RKV_STAMP(tid == 0, 24);
+        if (K > 0 && tid < kWave) wave_topk_lds(pkey_s, NP, K, emit);
     } else {
         for (int p = tid; p < NP; p += kBlock) blk_s[p] = a.page_table[(int64_t)b * max_pages + p];
         if (append && tid < D && slot != 0) {

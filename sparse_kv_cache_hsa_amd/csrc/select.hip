@@ -196,8 +196,7 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
         }
     }
     lds_barrier();
-    rank_channels<D, G, kSelBlock>(qs, k1, comp_s, cnt_s, ch_s, qsel, wave_tot,
-                                       kPacked ? qpm_s : nullptr);
+    rank_channels_wave<D, G>(qs, k1, ch_s, qsel, kPacked ? qpm_s : nullptr);
     if (a.chan_out && ck == 0 && tid < k1) a.chan_out[bh * k1 + tid] = ch_s[tid];
     constexpr int V = 16 / (int)sizeof(T);
     if (2 * k1 * ((cnt + V - 1) / V * V) <= kStageElems) {

@@ -19,6 +19,8 @@
 // unsigned 64-bit compare.
 #pragma once
 
+#include <type_traits>
+
 #include "rkv_internal.h"
 
 namespace rkv {
@@ -85,36 +87,154 @@ __device__ __forceinline__ K wave_sort_desc(K key) {
     return key;
 }
 
-// Top-K for K <= 64 of n <= BLOCK composite keys, key i held by thread i
-// (threads >= n pass 0, below every real key).  The waves holding keys sort
-// them into sorted_s (LDS, n rounded up to 64 uint64); after one barrier
-// wave 0 folds the sorted lists into the 64 largest keys (the element-wise
-// maximum of a descending list and a reversed one is bitonic and holds the
-// 64 largest of both), then sorts the K winners by index and calls
-// emit(pos, i) on its lanes pos < K, i ascending.  All threads must call it;
-// the caller synchronises the block before using what emit wrote.
-template <int BLOCK, typename Emit>
-__device__ void topk_small(uint64_t key, int n, int K, uint64_t *sorted_s, Emit emit) {
-    const int tid = threadIdx.x, w = tid / kWave, lane = tid & (kWave - 1);
-    const int nw = (n + kWave - 1) / kWave;
-    if (w < nw) {
-        key = wave_sort_desc(key);
-        if (w > 0) sorted_s[tid] = key;
+// ---- top-k inside one wave by a ballot threshold search ---------------------
+// The keys are unsigned words held by the 64 lanes of one wave, E slots per
+// lane: slot e of lane l holds the key of index e*64 + l, for indices below n;
+// every other slot must hold 0.  A threshold T with at least K keys >= T
+// (1 <= K <= n) is raised bit by bit from the top, a bit kept whenever at
+// least K keys stay >= T (counted with ballots), until exactly K keys are
+// >= T or every bit is decided (T is then the K-th largest key).  The top K
+// by (key desc, index asc) are the keys > T and the lowest-indexed keys equal
+// to T; emit(pos, index) writes them in ascending index order, so no sort is
+// needed.  Only the calling wave takes part; no barrier.
+template <int E, typename Emit>
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[E], int n, int K, Emit emit) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t below = lane ? (~0ull >> (kWave - lane)) : 0ull;
+    // The bits above the highest one in which two keys differ are common to
+    // all of them, so T starts with them (wave-wide OR and AND of the keys;
+    // the slots past n hold 0 and are left out of the AND).
+    uint32_t k_or = 0u, k_and = ~0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        k_or |= key[e];
+        if (e * kWave + lane < n) k_and &= key[e];
+    }
+    k_or |= lane_xor<1>(k_or);
+    k_and &= lane_xor<1>(k_and);
+    k_or |= lane_xor<2>(k_or);
+    k_and &= lane_xor<2>(k_and);
+    k_or |= lane_xor<4>(k_or);
+    k_and &= lane_xor<4>(k_and);
+    k_or |= lane_xor<8>(k_or);
+    k_and &= lane_xor<8>(k_and);
+    k_or |= lane_xor<16>(k_or);
+    k_and &= lane_xor<16>(k_and);
+    k_or |= lane_xor<32>(k_or);
+    k_and &= lane_xor<32>(k_and);
+    k_or = (uint32_t)__builtin_amdgcn_readfirstlane((int)k_or);
+    k_and = (uint32_t)__builtin_amdgcn_readfirstlane((int)k_and);
+    const uint32_t diff = k_or ^ k_and;
+    const int top = diff ? 31 - __builtin_clz(diff) : -1;
+    // all keys equal above bit `top` (all equal: top = -1, T is that key)
+    uint32_t T = top < 0 ? k_and : (top == 31 ? 0u : (k_and & ~((2u << top) - 1u)));
+    // Then bit by bit below that.  The slots past n hold 0 and never reach a
+    // candidate (every candidate is above 0), so the counting needs no
+    // guards.  All compares of a candidate are issued before any count reads
+    // them, so the scalar counts wait for the vector compares once.
+    // (in groups of four slots, which bounds the scalar registers held).
+    // The search stops early once exactly K keys are >= T: they are then the
+    // top K whatever the lower bits of T, and the selection below takes them
+    // all (count(key > T) + count(key == T) = K).
+    constexpr int GS = E < 4 ? E : 4;
+    int cnt_T = n;  // count(key >= T)
+    for (int bit = top; bit >= 0 && cnt_T != K; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int e0 = 0; e0 < E; e0 += GS) {
+            uint64_t m[GS];
+#pragma unroll
+            for (int e = 0; e < GS; ++e) m[e] = __ballot(key[e0 + e] >= cand);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < GS; ++e) cnt += __popcll(m[e]);
+        }
+        if (cnt >= K) {
+            T = cand;
+            cnt_T = cnt;
+        }
+    }
+    int gt_tot = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) gt_tot += __popcll(__ballot(key[e] > T));
+    const int take_eq = K - gt_tot;
+    int base = 0, eq_seen = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (e * kWave >= n) break;
+        const bool valid = e * kWave + lane < n;
+        const bool eq = valid && key[e] == T;
+        const uint64_t em = __ballot(eq);
+        const bool sel = (valid && key[e] > T) || (eq && eq_seen + __popcll(em & below) < take_eq);
+        const uint64_t sm = __ballot(sel);
+        if (sel) emit(base + __popcll(sm & below), e * kWave + lane);
+        base += __popcll(sm);
+        eq_seen += __popcll(em);
+    }
+}
+
+// wave_topk over n <= 16 * 64 keys in LDS (keys_s[i] for i < n; entries
+// from n up to the next multiple of 64 must be 0), run by the calling wave
+// with the smallest slot count that holds them.
+template <typename Emit>
+__device__ __forceinline__ void wave_topk_lds(const uint32_t *keys_s, int n, int K, Emit emit) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int ne = (n + kWave - 1) / kWave;
+    auto run = [&](auto tag) {
+        constexpr int E = decltype(tag)::value;
+        uint32_t key[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) key[e] = e < ne ? keys_s[e * kWave + lane] : 0u;
+        wave_topk<E>(key, n, K, emit);
+    };
+    if (ne <= 1) run(std::integral_constant<int, 1>{});
+    else if (ne <= 2) run(std::integral_constant<int, 2>{});
+    else if (ne <= 4) run(std::integral_constant<int, 4>{});
+    else if (ne <= 8) run(std::integral_constant<int, 8>{});
+    else run(std::integral_constant<int, 16>{});
+}
+
+// Channel ranking by the block's first wave (the work is 2*D small ballot
+// steps, cheaper than spreading it over the block and synchronising).  qs
+// must be visible to the block.  On return ch_s[0..k1) holds the chosen
+// channels in ascending order and qsel[j][i] = qs[j][ch_s[i]]; if qpm is
+// given (bf16 queries), also the sign-split queries of staged_bound_exact,
+// qpm[i * 2G + j] = max(q, 0) and qpm[i * 2G + G + j] = min(q, 0) for
+// q = qsel[j][i].  All threads must call it; ends with a block barrier.
+template <int D, int G>
+__device__ __forceinline__ void rank_channels_wave(const float (*qs)[D], int k1, int *ch_s,
+                                                   float (*qsel)[D], float *qpm = nullptr) {
+    static_assert(D % kWave == 0, "head_dim");
+    constexpr int E = D / kWave;
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        uint32_t key[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < G; ++j) acc = acc + fabsf(qs[j][e * kWave + lane]);
+            // acc >= +0, so its bits order like its value
+            key[e] = __float_as_uint(acc);
+        }
+        wave_topk<E>(key, D, k1, [&](int o, int c) {
+            ch_s[o] = c;
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float qv = qs[j][c];
+                qsel[j][o] = qv;
+                if (qpm) {
+                    // by sign bit, so -0 goes to the Kmin side (both sides
+                    // give a zero product there)
+                    const bool neg = __float_as_uint(qv) >> 31;
+                    qpm[o * 2 * G + j] = neg ? 0.0f : qv;
+                    qpm[o * 2 * G + G + j] = neg ? qv : 0.0f;
+                }
+            }
+        });
     }
     lds_barrier();
-    if (w == 0) {
-        uint64_t top = key;
-        for (int l = 1; l < nw; ++l) {
-            const uint64_t other = sorted_s[l * kWave + (kWave - 1 - lane)];
-            top = other > top ? other : top;
-            top = bitonic_clean<32>(top, lane);
-        }
-        // ~index of the K winners, descending = index ascending; the other
-        // lanes carry 0 and sort last
-        uint32_t inv = lane < K ? (uint32_t)top : 0u;
-        inv = wave_sort_desc(inv);
-        if (lane < K) emit(lane, (int)~inv);
-    }
 }
 
 // Rank count for n <= BLOCK composite keys comp_s[0..n) (LDS): cnt_s[i] =
@@ -158,52 +278,6 @@ __device__ void rank_topk(const uint64_t *comp_s, int n, int K, int *cnt_s, int 
     int tot;
     const int pos = block_excl_count<NW>(sel, wave_tot, tot);
     if (sel) emit(pos, tid);
-}
-
-// Channel ranking.  qs must be visible to the block.  On return ch_s[0..k1)
-// holds the chosen channels in ascending order and qsel[j][i] = qs[j][ch_s[i]]
-// (both visible to the block); if qpm is given (bf16 queries), also the
-// sign-split queries of staged_bound_exact, qpm[i * 2G + j] = max(q, 0) and
-// qpm[i * 2G + G + j] = min(q, 0) for q = qsel[j][i].  comp_s: LDS scratch
-// of D uint64, cnt_s of D ints.  Requires D <= BLOCK.
-template <int D, int G, int BLOCK>
-__device__ __forceinline__ void rank_channels(const float (*qs)[D], int k1, uint64_t *comp_s,
-                                              int *cnt_s, int *ch_s, float (*qsel)[D],
-                                              int *wave_tot, float *qpm = nullptr) {
-    const int tid = threadIdx.x;
-    uint64_t key = 0;
-    if (tid < D) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < G; ++j) acc = acc + fabsf(qs[j][tid]);
-        // acc >= +0, so its bits order like its value
-        key = composite_key(__float_as_uint(acc), tid);
-    }
-    auto emit = [&](int o, int c) {
-        ch_s[o] = c;
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const float qv = qs[j][c];
-            qsel[j][o] = qv;
-            if (qpm) {
-                // by sign bit, so -0 goes to the Kmin side (both sides give
-                // a zero product there)
-                const bool neg = __float_as_uint(qv) >> 31;
-                qpm[o * 2 * G + j] = neg ? 0.0f : qv;
-                qpm[o * 2 * G + G + j] = neg ? qv : 0.0f;
-            }
-        }
-    };
-    // Wide blocks spread the all-pairs rank count over 4+ threads per key,
-    // which beats the single-wave merge of the per-wave sorts.
-    if (k1 <= kWave && BLOCK < 4 * D) {
-        topk_small<BLOCK>(key, D, k1, comp_s, emit);
-    } else {
-        if (tid < D) comp_s[tid] = key;
-        lds_barrier();
-        rank_topk<BLOCK>(comp_s, D, k1, cnt_s, wave_tot, emit);
-    }
-    lds_barrier();
 }
 
 // Page bound S(p).  smax/smin point at channel 0 of the (b, h) summaries;
@@ -417,43 +491,6 @@ __device__ __forceinline__ float staged_bound_exact(const uint16_t *stage, int n
 #pragma unroll
     for (int j = 0; j < G; ++j) tot = tot + s[j];
     return tot;
-}
-
-// Top-K of n <= BLOCK composite keys, key i held by thread i (threads >= n
-// pass 0, below every real key).  Every wave sorts its keys into LDS
-// (sorted_s: BLOCK uint64); the rank of a key is the number of larger keys in
-// all sorted lists, found by binary searches that advance over every list in
-// the same step; emit(pos, i) for the K largest, i ascending.  All threads
-// must call it.
-template <int BLOCK, typename Emit>
-__device__ void sort_topk(uint64_t key, int n, int K, uint64_t *sorted_s, int *wave_tot,
-                          Emit emit) {
-    constexpr int NW = BLOCK / kWave;
-    const int tid = threadIdx.x, w = tid / kWave;
-    const int nw = (n + kWave - 1) / kWave;  // waves holding real keys
-    if (w < nw) sorted_s[tid] = wave_sort_desc(key);
-    lds_barrier();
-    bool sel = false;
-    if (tid < n) {
-        // c[l] = number of entries > key in the descending list l
-        int c[NW];
-#pragma unroll
-        for (int l = 0; l < NW; ++l) c[l] = 0;
-#pragma unroll
-        for (int step = kWave / 2; step > 0; step >>= 1) {
-#pragma unroll
-            for (int l = 0; l < NW; ++l)
-                if (l < nw && sorted_s[l * kWave + c[l] + step - 1] > key) c[l] += step;
-        }
-        int rank = 0;
-#pragma unroll
-        for (int l = 0; l < NW; ++l)
-            if (l < nw) rank += c[l] + (c[l] == kWave - 1 && sorted_s[l * kWave + kWave - 1] > key);
-        sel = rank < K;
-    }
-    int tot;
-    const int pos = block_excl_count<NW>(sel, wave_tot, tot);
-    if (sel) emit(pos, tid);
 }
 
 }  // namespace rkv

@@ -62,22 +62,30 @@ class rkv_paged_cache(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32)]
 
 
+RKV_TRACE_SLOTS = 32
+
+
 class rkv_opts(ctypes.Structure):
     _fields_ = [("form", ctypes.c_int32), ("splitk_blocks", ctypes.c_int32),
                 ("select_chunk", ctypes.c_int32), ("select_radix", ctypes.c_int32),
                 ("attend_variant", ctypes.c_int32), ("attend_pages", ctypes.c_int32),
-                ("status", ctypes.c_void_p)]
+                ("status", ctypes.c_void_p), ("trace", ctypes.c_void_p)]
 
 
 def make_opts(form: int = RKV_FORM_AUTO, splitk_blocks: int = 0, select_chunk: int = 0,
               select_radix: int = 0, attend_variant: int = 0, attend_pages: int = 0,
-              status: torch.Tensor | None = None) -> rkv_opts:
+              status: torch.Tensor | None = None,
+              trace: torch.Tensor | None = None) -> rkv_opts:
     """Execution options (include/rkv.h rkv_opts).  status: optional device
-    int32 tensor of one element that receives RKV_DEV_* flags."""
+    int32 tensor of one element that receives RKV_DEV_* flags.  trace:
+    optional device int64 tensor of RKV_TRACE_SLOTS stamps per block, written
+    only by the phase-timing build."""
     if status is not None:
         _need(status, "status", torch.int32)
+    if trace is not None:
+        _need(trace, "trace", torch.int64)
     return rkv_opts(int(form), int(splitk_blocks), int(select_chunk), int(select_radix),
-                    int(attend_variant), int(attend_pages), _ptr(status))
+                    int(attend_variant), int(attend_pages), _ptr(status), _ptr(trace))
 
 
 def _opt(o: rkv_opts | None):

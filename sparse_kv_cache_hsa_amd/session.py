@@ -58,6 +58,8 @@ class Session:
         self.out = torch.zeros((self.B, self.Hq, self.d), dtype=torch.float32, device=self.dev)
         self.page_idx = [torch.zeros((self.B, self.Hkv, wl.k2), dtype=torch.int32,
                                      device=self.dev) for _ in range(self.n_layers)]
+        # execution options of every decode call, per layer (None = automatic)
+        self.opts = [None] * self.n_layers
 
     # ---- prefill -----------------------------------------------------------
     def prompt_batch(self, layer: int):
@@ -146,7 +148,7 @@ class Session:
             k, v, q = per_layer[l]
             rkv.rkv_decode_step(self.g, q, k, v, self.caches[l], n_new, self.summ[l],
                                 self.wl.k1, self.wl.k2, self.scale, self.out, self.ws,
-                                page_idx=self.page_idx[l])
+                                page_idx=self.page_idx[l], opts=self.opts[l])
 
     def advance(self, steps: int):
         self.rows = [r + steps for r in self.rows]
