@@ -53,6 +53,8 @@ extern "C" {
 #define RKV_ECAPACITY (-3)    /* rows do not fit the cache / page table */
 #define RKV_EUNSUPPORTED (-4) /* shape or dtype the library has no kernel for */
 #define RKV_EHIP (-5)         /* a HIP launch reported an error */
+#define RKV_ESCRATCH (-6)     /* rkv_decode_step_static: the shapes need more than the
+                                 library's static scratch (RKV_STATIC_SCRATCH_BYTES) */
 
 /* ---- element types ----------------------------------------------------- */
 #define RKV_F32 0
@@ -369,6 +371,29 @@ int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
                     float scale, float *out, int32_t *chan_idx, int32_t *page_idx,
                     float *page_scores, void *ws, size_t ws_bytes, void *stream,
                    const rkv_opts *opts);
+
+/* ---- the same step without a caller workspace ------------------------------ */
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * rkv_decode_step, but the workspace is a static device array of
+ * RKV_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  Nothing is allocated or freed by this call.
+ * The array's address on the current device is looked up on the first call
+ * on that device.  Every call on one GPU shares that GPU's array, so calls
+ * that may overlap on one GPU (different streams, or host threads without
+ * ordering) race and must not be issued; calls ordered on one stream are
+ * fine.  The array's contents are whatever the last call left; the decode
+ * kernels write every part they read, so nothing needs clearing.
+ * Errors: as rkv_decode_step, plus RKV_ESCRATCH when
+ * rkv_hsa_workspace_bytes(g, B, P, max_pages, k1, k2, opts) exceeds
+ * RKV_STATIC_SCRATCH_BYTES, and RKV_EHIP when the array's address cannot be
+ * obtained. */
+#define RKV_STATIC_SCRATCH_BYTES (16u << 20)
+int rkv_decode_step_static(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
+                           const void *k_new, const void *v_new, const rkv_paged_cache *cache,
+                           const int32_t *seq_lens, void *summaries, int32_t k1, int32_t k2,
+                           float scale, float *out, int32_t *chan_idx, int32_t *page_idx,
+                           float *page_scores, void *stream, const rkv_opts *opts);
 
 #ifdef __cplusplus
 } /* extern "C" */

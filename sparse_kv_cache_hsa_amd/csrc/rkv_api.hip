@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "rkv_internal.h"
 
 #ifndef RKV_BUILD_ID
@@ -10,6 +12,11 @@
 #endif
 
 using namespace rkv;
+
+// The workspace of rkv_decode_step_static.  In host code `scratch` names a
+// host-side stand-in, never the device array: its device address is looked
+// up per device with hipGetSymbolAddress and only that address is used.
+static __device__ __align__(256) unsigned char scratch[RKV_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -68,6 +75,31 @@ HsaWs hsa_ws(const rkv_gqa &g, int B, int P, int max_pages, int k2, const Knobs 
     return w;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up once per
+// device), or nullptr with *st set on failure.
+void *static_scratch(int *st) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *st = RKV_EHIP;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            *st = RKV_EHIP;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,6 +112,7 @@ const char *rkv_status_string(int status) {
         case RKV_ECAPACITY: return "rows do not fit the paged cache";
         case RKV_EUNSUPPORTED: return "unsupported shape or dtype";
         case RKV_EHIP: return "HIP launch error";
+        case RKV_ESCRATCH: return "shapes need more than the static scratch holds";
     }
     return "unknown status";
 }
@@ -312,6 +345,25 @@ int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
     if (st != RKV_OK) return st;
     return launch_attend(*g, dtype, B, q, *cache, seq_lens, page_idx, k2, scale, out,
                          base + w.select, kn, s);
+}
+
+int rkv_decode_step_static(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
+                           const void *k_new, const void *v_new, const rkv_paged_cache *cache,
+                           const int32_t *seq_lens, void *summaries, int32_t k1, int32_t k2,
+                           float scale, float *out, int32_t *chan_idx, int32_t *page_idx,
+                           float *page_scores, void *stream, const rkv_opts *opts) {
+    clear_pending_error();
+    int st = check_gqa(g);
+    if (st != RKV_OK) return st;
+    if ((st = check_cache(cache)) != RKV_OK) return st;
+    st = check_select_args(g, dtype, B, q, seq_lens, cache->page_size, cache->max_pages, k1, k2);
+    if (st != RKV_OK) return st;
+    const size_t need = hsa_ws(*g, B, cache->page_size, cache->max_pages, k2, knobs_of(opts)).total;
+    if (need > (size_t)RKV_STATIC_SCRATCH_BYTES) return RKV_ESCRATCH;
+    void *ws = static_scratch(&st);
+    if (!ws) return st;
+    return rkv_decode_step(g, dtype, B, q, k_new, v_new, cache, seq_lens, summaries, k1, k2, scale,
+                           out, chan_idx, page_idx, page_scores, ws, need, stream, opts);
 }
 
 int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,

@@ -24,6 +24,8 @@ RKV_EWORKSPACE = -2
 RKV_ECAPACITY = -3
 RKV_EUNSUPPORTED = -4
 RKV_EHIP = -5
+RKV_ESCRATCH = -6
+RKV_STATIC_SCRATCH_BYTES = 16 << 20
 RKV_F32 = 0
 RKV_BF16 = 1
 RKV_MAX_K2 = 1024
@@ -41,7 +43,7 @@ EXPORTED = (
     "rkv_prefill_evict_workspace_bytes", "rkv_prefill_evict", "rkv_append_summaries",
     "rkv_hsa_workspace_bytes", "rkv_hsa_select", "rkv_hsa_attend", "rkv_hsa_decode",
     "rkv_decode_step", "rkv_prefill_evict_chunk_workspace_bytes", "rkv_prefill_evict_chunk",
-    "rkv_decode_mode",
+    "rkv_decode_mode", "rkv_decode_step_static",
 )
 
 
@@ -144,6 +146,9 @@ def load_library(path: str | None = None, check_build_id: bool = True):
         lib.rkv_decode_step.argtypes = [G, i32, i32, vp, vp, vp, C, vp, vp, i32, i32, f32, vp,
                                         vp, vp, vp, vp, sz, vp, O]
         lib.rkv_decode_step.restype = ctypes.c_int
+        lib.rkv_decode_step_static.argtypes = [G, i32, i32, vp, vp, vp, C, vp, vp, i32, i32, f32,
+                                               vp, vp, vp, vp, vp, O]
+        lib.rkv_decode_step_static.restype = ctypes.c_int
         if check_build_id:
             built = lib.rkv_build_id().decode()
             want = _build.source_hash()
@@ -444,3 +449,29 @@ def rkv_decode_step(g: rkv_gqa, q: torch.Tensor, k_new: torch.Tensor | None,
         _ptr(v_new), ctypes.byref(cs), seq_lens.data_ptr(), summaries.data_ptr(), int(k1),
         int(k2), float(scale), out.data_ptr(), _ptr(chan_idx), _ptr(page_idx),
         _ptr(page_scores), ws.data_ptr(), ws.numel(), _stream(), _opt(opts)))
+
+
+def rkv_decode_step_static(g: rkv_gqa, q: torch.Tensor, k_new: torch.Tensor | None,
+                           v_new: torch.Tensor | None, cache: PagedCache, seq_lens: torch.Tensor,
+                           summaries: torch.Tensor, k1: int, k2: int, scale: float,
+                           out: torch.Tensor, chan_idx: torch.Tensor | None = None,
+                           page_idx: torch.Tensor | None = None,
+                           page_scores: torch.Tensor | None = None,
+                           opts: rkv_opts | None = None) -> None:
+    """rkv_decode_step with the library's static device scratch as the
+    workspace (no allocation; calls that overlap on one GPU race)."""
+    _need(q, "q", cache.k_pool.dtype)
+    _need(k_new, "k_new", q.dtype, optional=True)
+    _need(v_new, "v_new", q.dtype, optional=True)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(summaries, "summaries", q.dtype)
+    _need(out, "out", torch.float32)
+    _need(chan_idx, "chan_idx", torch.int32, optional=True)
+    _need(page_idx, "page_idx", torch.int32, optional=True)
+    _need(page_scores, "page_scores", torch.float32, optional=True)
+    cs = cache.c_struct()
+    _check("rkv_decode_step_static", load_library().rkv_decode_step_static(
+        ctypes.byref(g), _dtype_code(q), int(q.shape[0]), q.data_ptr(), _ptr(k_new),
+        _ptr(v_new), ctypes.byref(cs), seq_lens.data_ptr(), summaries.data_ptr(), int(k1),
+        int(k2), float(scale), out.data_ptr(), _ptr(chan_idx), _ptr(page_idx),
+        _ptr(page_scores), _stream(), _opt(opts)))

@@ -196,3 +196,24 @@ def test_no_environment_lookups_in_the_library():
     for name in os.listdir(csrc):
         text = open(os.path.join(csrc, name)).read()
         assert "getenv" not in text and "environ" not in text, name
+
+
+def test_static_decode_rejects_oversized_shapes(rkv_lib):
+    """rkv_decode_step_static refuses shapes whose workspace exceeds the
+    static scratch (before any device work)."""
+    L = rkv_lib
+    lib = L.load_library()
+    g = L.gqa(8, 4, 128)
+    B, P, max_pages, k1, k2 = 4096, 16, 4096, 32, 1024
+    assert L.rkv_hsa_workspace_bytes(g, B, P, max_pages, k1, k2) > L.RKV_STATIC_SCRATCH_BYTES
+    fake = 0x10000  # never dereferenced: the size check fails first
+    cache = L.rkv_paged_cache(fake, fake, fake, 64, P, max_pages)
+    st = lib.rkv_decode_step_static(ctypes.byref(g), L.RKV_BF16, B, fake, None, None,
+                                    ctypes.byref(cache), fake, fake, k1, k2, 0.1, fake, None,
+                                    None, None, None, None)
+    assert st == L.RKV_ESCRATCH
+    assert lib.rkv_status_string(st).decode().startswith("shapes need more")
+    # argument errors still come first
+    assert lib.rkv_decode_step_static(None, L.RKV_BF16, 1, fake, None, None, ctypes.byref(cache),
+                                      fake, fake, k1, 8, 0.1, fake, None, None, None, None,
+                                      None) == L.RKV_EINVAL
