@@ -179,6 +179,26 @@ def snapkv_chunked_group(q_wins, k_chunks, pool_kernel: int, keeps, scale: float
     return out
 
 
+def mt_turn_view(q_win: np.ndarray, k_hist: np.ndarray, pool_kernel: int, keep: int,
+                 scale: float):
+    """RocketKV-MT's per-turn candidate view for one KV head group.
+
+    "RocketKV: Accelerating Long-Context LLM Inference via Two-Stage KV Cache
+    Compression" (atlas.scime.ai), "Approach" and "Limitations": RocketKV-MT
+    retains the tokens stage 1 would evict for later turns, so it saves
+    memory traffic but no KV storage; "RocketKV-adapted -- Two-Stage
+    Compression", "Should you use this?": it skips permanent eviction so that
+    earlier-turn tokens survive.  Reading (the pages give no per-turn rule):
+    at the start of a turn, after the turn's rows are appended to the full
+    history k_hist [L, d] (never shortened), SnapKV++ scores the whole
+    history with the turn's last w queries q_win [G, w, d] and keeps `keep`
+    rows; those rows, in ascending position, are the turn's view that HSA
+    decodes over; nothing is deleted, so a row left out of one turn's view
+    can be in the next one's.  Returns (kept, pooled) as snapkv_group."""
+    kept, _, pooled = snapkv_group(q_win, k_hist, pool_kernel, keep, scale)
+    return kept, pooled
+
+
 def hsa_group(q: np.ndarray, k: np.ndarray, v: np.ndarray, smax: np.ndarray,
               smin: np.ndarray, n: int, P: int, k1: int, k2: int, scale: float):
     """HSA decode for one KV head group.  q [G, d]; k, v [>=n, d]; summaries
