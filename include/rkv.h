@@ -254,6 +254,40 @@ int rkv_prefill_evict_chunk(const rkv_gqa *g, int32_t dtype, int32_t B,
                             void *ws, size_t ws_bytes, void *stream,
                    const rkv_opts *opts);
 
+/* ---- multi-turn view (RocketKV-MT) ----------------------------------------- */
+/* [P1] "Approach" and "Limitations": RocketKV-MT retains the tokens stage 1
+ * would evict for later turns (memory-traffic savings only); [P3] "Should you
+ * use this?": it skips permanent eviction so that earlier-turn tokens
+ * survive.  Reading: at the start of a turn, with the turn's rows already
+ * appended to the full cache, SnapKV++ (as rkv_prefill_evict) scores the
+ * first n_rows[b] rows of `full` with the turn's last w queries and keeps
+ * keep[b] of them; the kept rows, in ascending position, are written to
+ * logical rows [0, min(keep, n)) of `view` and the view's summaries are
+ * rebuilt.  HSA then decodes over the view for the turn.  `full` is only
+ * read: nothing is deleted, so a row left out of one turn's view can be in
+ * the next one's.
+ *   n_rows, keep  : host [B]; keep >= w and n_rows >= w unless keep >= n_rows
+ *                   (the view is then the whole history).
+ *   q_win         : device [B][Hq][w][d], the turn's last w queries (query i
+ *                   at position n - w + i).
+ *   full          : the retained history, n_rows <= capacity.
+ *   view          : destination, needs min(keep, n) <= capacity; its blocks
+ *                   must not overlap those of full's first n rows.
+ *   view_summaries: device [B][Hkv][2][d][view max_pages], optional.
+ *   kept_idx, keep_stride, pooled_scores, view_lens_out : as rkv_prefill_evict
+ *                   (positions in the full history; pooled_scores
+ *                   [B][Hkv][max n]).
+ *   ws, ws_bytes  : rkv_turn_filter_workspace_bytes(g, B, max n, w).
+ * Errors: RKV_EINVAL, RKV_EUNSUPPORTED, RKV_ECAPACITY, RKV_EWORKSPACE,
+ * RKV_EHIP. */
+size_t rkv_turn_filter_workspace_bytes(const rkv_gqa *g, int32_t B, int64_t L_max, int32_t w);
+int rkv_turn_filter(const rkv_gqa *g, int32_t dtype, int32_t B, const int32_t *n_rows,
+                    const int32_t *keep, int32_t w, int32_t pool_kernel, float scale,
+                    const void *q_win, const rkv_paged_cache *full, const rkv_paged_cache *view,
+                    void *view_summaries, int32_t *kept_idx, int32_t keep_stride,
+                    float *pooled_scores, int32_t *view_lens_out, void *ws, size_t ws_bytes,
+                    void *stream, const rkv_opts *opts);
+
 /* ---- incremental page-summary append ------------------------------------ */
 /* [P3] "Where it sits" (paged max/min) and "Evidence" (incremental update
  * == rebuild).  For every sequence b, rows [n_old[b], n_new[b]) are folded

@@ -628,20 +628,20 @@ size_t evict_chunk_ws_bytes(const rkv_gqa &g, int B, int64_t L_max, int w) {
 int launch_evict_chunk(const rkv_gqa &g, int dtype, int B, const ChunkSeq &cs, const EvictSeq &seq,
                        int64_t L_max, int64_t C_max, int w, int pool_kernel, float scale,
                        const void *q_win, const void *k_chunk, const void *v_chunk,
-                       const rkv_paged_cache &c, void *summaries, int32_t *kept_idx,
-                       int keep_stride, float *pooled, int32_t *seq_lens_out, void *ws,
-                       int32_t *status, hipStream_t s) {
+                       const rkv_paged_cache &src, const rkv_paged_cache &c, void *summaries,
+                       int32_t *kept_idx, int keep_stride, float *pooled, int32_t *seq_lens_out,
+                       void *ws, int32_t *status, hipStream_t s) {
     char *base = (char *)ws;
     void *k_cat = base, *v_cat = base + cat_bytes(g, B, L_max);
     void *ews = base + 2 * cat_bytes(g, B, L_max);
     const int d = g.head_dim;
     if (dtype == RKV_F32) {
-        if (d == 64) launch_concat<float, 64>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, status, s);
-        else if (d == 128) launch_concat<float, 128>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, status, s);
+        if (d == 64) launch_concat<float, 64>(g, B, cs, L_max, k_chunk, v_chunk, C_max, src, k_cat, v_cat, status, s);
+        else if (d == 128) launch_concat<float, 128>(g, B, cs, L_max, k_chunk, v_chunk, C_max, src, k_cat, v_cat, status, s);
         else return RKV_EUNSUPPORTED;
     } else {
-        if (d == 64) launch_concat<uint16_t, 64>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, status, s);
-        else if (d == 128) launch_concat<uint16_t, 128>(g, B, cs, L_max, k_chunk, v_chunk, C_max, c, k_cat, v_cat, status, s);
+        if (d == 64) launch_concat<uint16_t, 64>(g, B, cs, L_max, k_chunk, v_chunk, C_max, src, k_cat, v_cat, status, s);
+        else if (d == 128) launch_concat<uint16_t, 128>(g, B, cs, L_max, k_chunk, v_chunk, C_max, src, k_cat, v_cat, status, s);
         else return RKV_EUNSUPPORTED;
     }
     const int st = launch_status();

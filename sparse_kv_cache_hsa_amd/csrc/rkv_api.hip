@@ -234,9 +234,59 @@ int rkv_prefill_evict_chunk(const rkv_gqa *g, int32_t dtype, int32_t B,
     const size_t need = evict_chunk_ws_bytes(*g, B, L_max, w);
     if (!ws || ws_bytes < need) return RKV_EWORKSPACE;
     return launch_evict_chunk(*g, dtype, B, cs, seq, L_max, C_max, w, pool_kernel, scale, q_win,
-                              k_chunk, v_chunk, *cache, summaries, kept_idx, keep_stride,
+                              k_chunk, v_chunk, *cache, *cache, summaries, kept_idx, keep_stride,
                               pooled_scores, seq_lens_out, ws, knobs_of(opts).status,
                               (hipStream_t)stream);
+}
+
+size_t rkv_turn_filter_workspace_bytes(const rkv_gqa *g, int32_t B, int64_t L_max, int32_t w) {
+    if (check_gqa(g) != RKV_OK || B < 1 || L_max < 1 || w < 1) return 0;
+    return evict_chunk_ws_bytes(*g, B, L_max, w);
+}
+
+int rkv_turn_filter(const rkv_gqa *g, int32_t dtype, int32_t B, const int32_t *n_rows,
+                    const int32_t *keep, int32_t w, int32_t pool_kernel, float scale,
+                    const void *q_win, const rkv_paged_cache *full, const rkv_paged_cache *view,
+                    void *view_summaries, int32_t *kept_idx, int32_t keep_stride,
+                    float *pooled_scores, int32_t *view_lens_out, void *ws, size_t ws_bytes,
+                    void *stream, const rkv_opts *opts) {
+    clear_pending_error();
+    int st = check_gqa(g);
+    if (st != RKV_OK) return st;
+    if ((st = check_dtype(dtype)) != RKV_OK) return st;
+    if (B < 1 || !n_rows || !keep || !q_win) return RKV_EINVAL;
+    if (B > RKV_MAX_EVICT_BATCH) return RKV_EUNSUPPORTED;
+    if (w < 1 || pool_kernel < 1 || (pool_kernel % 2) == 0) return RKV_EINVAL;
+    if (!(scale > 0.0f) || !isfinite(scale)) return RKV_EINVAL;
+    if ((st = check_cache(full)) != RKV_OK) return st;
+    if ((st = check_cache(view)) != RKV_OK) return st;
+    const int64_t cap_full = (int64_t)full->max_pages * full->page_size;
+    const int64_t cap_view = (int64_t)view->max_pages * view->page_size;
+    ChunkSeq cs;
+    EvictSeq seq;
+    memset(&cs, 0, sizeof cs);
+    memset(&seq, 0, sizeof seq);
+    int64_t L_max = 1, keep_rows = 0;
+    for (int b = 0; b < B; ++b) {
+        const int32_t n = n_rows[b], kp = keep[b];
+        if (n < 0 || kp < 0) return RKV_EINVAL;
+        if (n > cap_full) return RKV_ECAPACITY;
+        if (kp < n && (kp < w || n < w)) return RKV_EINVAL;
+        const int64_t ke = kp < n ? kp : n;
+        if (ke > cap_view) return RKV_ECAPACITY;
+        if (ke > keep_rows) keep_rows = ke;
+        if (n > L_max) L_max = n;
+        cs.n_cached[b] = n;
+        cs.L[b] = n;
+        seq.L[b] = n;
+        seq.keep[b] = kp;
+    }
+    if (kept_idx && keep_stride < keep_rows) return RKV_EINVAL;
+    if (!ws || ws_bytes < evict_chunk_ws_bytes(*g, B, L_max, w)) return RKV_EWORKSPACE;
+    return launch_evict_chunk(*g, dtype, B, cs, seq, L_max, 1, w, pool_kernel, scale, q_win,
+                              nullptr, nullptr, *full, *view, view_summaries, kept_idx,
+                              keep_stride, pooled_scores, view_lens_out, ws,
+                              knobs_of(opts).status, (hipStream_t)stream);
 }
 
 int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,

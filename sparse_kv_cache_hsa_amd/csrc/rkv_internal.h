@@ -409,12 +409,17 @@ struct ChunkSeq {
     int32_t L[RKV_MAX_EVICT_BATCH];  // n_cached + chunk_len
 };
 size_t evict_chunk_ws_bytes(const rkv_gqa &g, int B, int64_t L_max, int w);
+// The rows [0, n_cached) of `src` followed by the chunk's rows are copied
+// into the workspace as one sequence, which is evicted into `c` (the kept
+// rows and their summaries).  src may be c (chunked prefill) or another cache
+// that is only read (the multi-turn view); k_chunk/v_chunk may be null when
+// every chunk is empty.
 int launch_evict_chunk(const rkv_gqa &g, int dtype, int B, const ChunkSeq &cs, const EvictSeq &seq,
                        int64_t L_max, int64_t C_max, int w, int pool_kernel, float scale,
                        const void *q_win, const void *k_chunk, const void *v_chunk,
-                       const rkv_paged_cache &c, void *summaries, int32_t *kept_idx,
-                       int keep_stride, float *pooled, int32_t *seq_lens_out, void *ws,
-                       int32_t *status, hipStream_t s);
+                       const rkv_paged_cache &src, const rkv_paged_cache &c, void *summaries,
+                       int32_t *kept_idx, int keep_stride, float *pooled, int32_t *seq_lens_out,
+                       void *ws, int32_t *status, hipStream_t s);
 int launch_evict(const rkv_gqa &g, int dtype, int B, const EvictSeq &seq, int64_t L_max,
                  int w, int pool_kernel, float scale, const void *q_win, const void *k,
                  const void *v, const rkv_paged_cache &c, void *summaries,

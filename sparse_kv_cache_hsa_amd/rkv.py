@@ -43,7 +43,8 @@ EXPORTED = (
     "rkv_prefill_evict_workspace_bytes", "rkv_prefill_evict", "rkv_append_summaries",
     "rkv_hsa_workspace_bytes", "rkv_hsa_select", "rkv_hsa_attend", "rkv_hsa_decode",
     "rkv_decode_step", "rkv_prefill_evict_chunk_workspace_bytes", "rkv_prefill_evict_chunk",
-    "rkv_decode_mode", "rkv_decode_step_static",
+    "rkv_decode_mode", "rkv_decode_step_static", "rkv_turn_filter_workspace_bytes",
+    "rkv_turn_filter",
 )
 
 
@@ -129,6 +130,11 @@ def load_library(path: str | None = None, check_build_id: bool = True):
                                                 i32, f32, vp, vp, vp, C, vp, vp, i32, vp, vp,
                                                 vp, sz, vp, O]
         lib.rkv_prefill_evict_chunk.restype = ctypes.c_int
+        lib.rkv_turn_filter_workspace_bytes.argtypes = [G, i32, i64, i32]
+        lib.rkv_turn_filter_workspace_bytes.restype = sz
+        lib.rkv_turn_filter.argtypes = [G, i32, i32, P(i32), P(i32), i32, i32, f32, vp, C, C, vp,
+                                        vp, i32, vp, vp, vp, sz, vp, O]
+        lib.rkv_turn_filter.restype = ctypes.c_int
         lib.rkv_append_summaries.argtypes = [G, i32, i32, C, vp, vp, i32, vp, vp, vp, vp, O]
         lib.rkv_append_summaries.restype = ctypes.c_int
         lib.rkv_hsa_workspace_bytes.argtypes = [G, i32, i32, i32, i32, i32, O]
@@ -335,6 +341,42 @@ def rkv_prefill_evict_chunk(g: rkv_gqa, n_cached, chunk_lens, keep, q_win: torch
         int(pool_kernel), float(scale), q_win.data_ptr(), k_chunk.data_ptr(),
         v_chunk.data_ptr(), ctypes.byref(cs), _ptr(summaries), _ptr(kept_idx), stride,
         _ptr(pooled_scores), _ptr(seq_lens_out), ws.data_ptr(), ws.numel(), _stream(), _opt(opts)))
+
+
+def rkv_turn_filter_workspace_bytes(g: rkv_gqa, B: int, L_max: int, w: int) -> int:
+    return int(load_library().rkv_turn_filter_workspace_bytes(ctypes.byref(g), B, L_max, w))
+
+
+def rkv_turn_filter(g: rkv_gqa, n_rows, keep, q_win: torch.Tensor, w: int, pool_kernel: int,
+                    scale: float, full: PagedCache, view: PagedCache,
+                    view_summaries: torch.Tensor | None = None,
+                    kept_idx: torch.Tensor | None = None,
+                    pooled_scores: torch.Tensor | None = None,
+                    view_lens_out: torch.Tensor | None = None,
+                    ws: torch.Tensor | None = None, opts: rkv_opts | None = None) -> None:
+    """RocketKV-MT's per-turn view: SnapKV++ over the first n_rows[b] rows of
+    `full` (only read) with the turn's last w queries q_win [B, Hq, w, d];
+    the kept rows go to `view`.  n_rows/keep: host sequences of ints."""
+    _need(q_win, "q_win", full.k_pool.dtype)
+    _need(view_summaries, "view_summaries", full.k_pool.dtype, optional=True)
+    _need(kept_idx, "kept_idx", torch.int32, optional=True)
+    _need(pooled_scores, "pooled_scores", torch.float32, optional=True)
+    _need(view_lens_out, "view_lens_out", torch.int32, optional=True)
+    B = int(q_win.shape[0])
+    nr = (ctypes.c_int32 * B)(*[int(x) for x in n_rows])
+    kp = (ctypes.c_int32 * B)(*[int(x) for x in keep])
+    if ws is None:
+        ws = torch.empty(rkv_turn_filter_workspace_bytes(g, B, max(1, max(int(x) for x in n_rows)),
+                                                         w), dtype=torch.uint8,
+                         device=q_win.device)
+    _need(ws, "ws")
+    fs, vs = full.c_struct(), view.c_struct()
+    stride = int(kept_idx.shape[-1]) if kept_idx is not None else 0
+    _check("rkv_turn_filter", load_library().rkv_turn_filter(
+        ctypes.byref(g), _dtype_code(q_win), B, nr, kp, int(w), int(pool_kernel), float(scale),
+        q_win.data_ptr(), ctypes.byref(fs), ctypes.byref(vs), _ptr(view_summaries),
+        _ptr(kept_idx), stride, _ptr(pooled_scores), _ptr(view_lens_out), ws.data_ptr(),
+        ws.numel(), _stream(), _opt(opts)))
 
 
 def rkv_append_summaries(g: rkv_gqa, cache: PagedCache, n_old: torch.Tensor,

@@ -217,3 +217,30 @@ def test_static_decode_rejects_oversized_shapes(rkv_lib):
     assert lib.rkv_decode_step_static(None, L.RKV_BF16, 1, fake, None, None, ctypes.byref(cache),
                                       fake, fake, k1, 8, 0.1, fake, None, None, None, None,
                                       None) == L.RKV_EINVAL
+
+
+def test_turn_filter_argument_checks(rkv_lib):
+    L = rkv_lib
+    lib = L.load_library()
+    g = L.gqa(2, 2, 64)
+    fake = 0x10000
+    full = L.rkv_paged_cache(fake, fake, fake, 64, 16, 20)   # 320 rows
+    view = L.rkv_paged_cache(fake, fake, fake, 64, 16, 4)    # 64 rows
+
+    def call(n_rows, keeps, w=8, pool=7, ws=1 << 30, stride=0):
+        B = len(n_rows)
+        arr = lambda xs: (ctypes.c_int32 * B)(*xs)
+        return lib.rkv_turn_filter(ctypes.byref(g), 0, B, arr(n_rows), arr(keeps), w, pool,
+                                   0.125, fake, ctypes.byref(full), ctypes.byref(view), None,
+                                   fake if stride else None, stride, None, None, fake, ws, None,
+                                   None)
+
+    assert call([200], [40], pool=4) == L.RKV_EINVAL       # even pooling kernel
+    assert call([200], [5]) == L.RKV_EINVAL                # keep below the window
+    assert call([400], [40]) == L.RKV_ECAPACITY            # history beyond the full cache
+    assert call([200], [80]) == L.RKV_ECAPACITY            # view beyond its capacity
+    # keep >= n copies the whole history, which must fit the view
+    assert call([70], [100]) == L.RKV_ECAPACITY
+    assert call([200], [40], stride=10) == L.RKV_EINVAL    # kept_idx row too short
+    assert call([200], [40], ws=100) == L.RKV_EWORKSPACE
+    assert L.rkv_turn_filter_workspace_bytes(g, 1, 320, 8) > 0
