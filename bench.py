@@ -81,7 +81,8 @@ def counted_traffic(kernel: str, workload: str, build_id: str):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none for
     this workload or it was taken on another build of the kernels."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    key = kernel.replace(" + ", "+").replace(" ", "-")
+    path = os.path.join(ROOT, "profiles", f"{key}_{workload}_counters.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -151,15 +152,132 @@ def cpu_baseline(wl, sess, budget_s: float, threads: int = 1):
                       f"{sess.n_layers} layers; {el:.1f} s on {threads} thread(s)"}
 
 
+def graph_of(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def turn_plan(sess, steps_per_turn: int, view_budget: int = 0):
+    """Inputs of every turn, generated before anything is timed: the turn's
+    append sources per layer, its decode-step inputs and, with a view budget,
+    the turn's window queries and view sizes.  Row counts are simulated and
+    restored, so the session is left as it was."""
+    rows0 = list(sess.rows)
+    plan = []
+    for t in range(sess.wl.turns):
+        tp = {"src": [sess.turn_source(l, t) for l in range(sess.n_layers)]}
+        sess.advance(sess.wl.turn_append)
+        if view_budget:
+            tp["keep"] = sess.turn_view_keep(view_budget)
+            tp["n_rows"] = list(sess.rows)
+            tp["qw"] = [sess.turn_window_q(l, t) for l in range(sess.n_layers)]
+            sess.view_rows = list(tp["keep"])
+            tp["steps"] = sess.make_view_inputs(steps_per_turn, t)
+        else:
+            tp["steps"] = sess.make_inputs(steps_per_turn, t)
+        sess.advance(steps_per_turn)
+        plan.append(tp)
+    sess.rows = rows0
+    return plan
+
+
+def run_turns(torch, sess, plan, use_graph: bool, view_ws=None):
+    """Runs every turn: the turn's append (and, with views, the per-turn
+    filter), then its decode steps; returns per-turn event times in ms and
+    the total.  Graphs are captured beforehand; their replays are timed."""
+    view = view_ws is not None
+    turns = []
+    for tp in plan:
+        def prologue(tp=tp):
+            saved = sess.rows
+            for l in range(sess.n_layers):
+                sess.append_source(l, tp["src"][l])
+            if view:
+                sess.rows = tp["n_rows"]
+                for l in range(sess.n_layers):
+                    sess.turn_filter(l, tp["qw"][l], tp["keep"], view_ws)
+                sess.rows = saved
+        step = sess.view_step if view else sess.step
+        if use_graph:
+            g_pro = graph_of(torch, prologue)
+            g_steps = [graph_of(torch, lambda i=i: step(i)) for i in tp["steps"]]
+            turns.append((g_pro.replay, [g.replay for g in g_steps], g_pro, g_steps))
+        else:
+            turns.append((prologue, [lambda i=i: step(i) for i in tp["steps"]]))
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in turns]
+    torch.cuda.synchronize()
+    for t, tr in enumerate(turns):
+        ev[t][0].record()
+        tr[0]()
+        ev[t][1].record()
+        for f in tr[1]:
+            f()
+        ev[t][2].record()
+    torch.cuda.synchronize()
+    pro = [e[0].elapsed_time(e[1]) for e in ev]
+    dec = [e[1].elapsed_time(e[2]) for e in ev]
+    total = ev[0][0].elapsed_time(ev[-1][2])
+    for tp in plan:
+        sess.advance(sess.wl.turn_append + len(tp["steps"]))
+    if view:
+        sess.view_rows = [k + len(plan[-1]["steps"]) for k in plan[-1]["keep"]]
+    return pro, dec, total
+
+
+def mt_filter_leg(torch, rkv, wl, args, dev, budget: int):
+    """RocketKV-MT on the multi-turn workload: per turn, append the turn's
+    rows to the full cache, re-run SnapKV++ over the whole history with the
+    turn's last w queries into a compacted view (stage 1's share of `budget`
+    under the adaptive split), then decode on the view while every new token
+    also goes to the full cache.  A session of its own; returns its report."""
+    from sparse_kv_cache_hsa_amd.session import Session
+    spt = args.steps // wl.turns
+    sess = Session(wl, extra_rows=args.warmup + max(0, spt - wl.decode_steps), device=dev)
+    for l in range(sess.n_layers):
+        sess.prefill_layer(l)
+    final = [n + wl.turns * (wl.turn_append + spt) for n in sess.rows]
+    most = max(rkv.rkv_split_ratio(n / budget, n, wl.window)[3] if n > budget else n
+               for n in final)
+    sess.enable_turn_view(most, spt + 1)
+    sess.rows = [n + wl.turns * wl.turn_append + (wl.turns - 1) * spt for n in sess.rows]
+    ws = sess.turn_filter_workspace()
+    sess.rows = [n - wl.turns * wl.turn_append - (wl.turns - 1) * spt for n in sess.rows]
+    plan = turn_plan(sess, spt, view_budget=budget)
+    torch.cuda.synchronize()
+    pro, dec, total = run_turns(torch, sess, plan, not args.no_graph, view_ws=ws)
+    K = spt * wl.turns
+    log(f"[bench] mt-filter: {K} steps over {wl.turns} turns in {total:.2f} ms; per turn "
+        f"append+filter {sum(pro) / len(pro):.3f} ms, decode {sum(dec) / len(dec):.3f} ms")
+    mode = rkv.decode_mode(sess.g, sess.B, sess.P, sess.view_max_pages, wl.k2, wl.k1,
+                           rkv.RKV_BF16 if wl.dtype.itemsize == 2 else rkv.RKV_F32)
+    return {"budget": budget, "view_rows_last_turn": plan[-1]["keep"],
+            "steps_per_s": round(K / (total * 1e-3), 3), "ms_per_step": round(total / K, 5),
+            "append_and_filter_ms_per_turn": [round(x, 4) for x in pro],
+            "decode_ms_per_turn": [round(x, 4) for x in dec],
+            "decode_us_per_step": round(sum(dec) * 1e3 / K, 3),
+            "view_path": FORMS[mode]}
+
+
+FORMS = {1: "standalone kernels", 2: "fused", 3: "fused split-K"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed decode steps (default 64; multi-turn workloads: every "
+                         "turn's steps, spread evenly over the turns)")
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-graph", action="store_true", help="enqueue steps eagerly")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--mt-filter", type=int, default=0, metavar="BUDGET",
+                    help="multi-turn workloads: also time RocketKV-MT's per-turn view at this "
+                         "total token budget (reported under mt_filter)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device to device 3 times (counter calibration)")
     args = ap.parse_args()
@@ -186,9 +304,15 @@ def main():
     wl = workloads.ALL[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    turns = wl.turns > 1
+    if args.steps is None:
+        args.steps = wl.turns * wl.decode_steps if turns else 64
     K, W = args.steps, args.warmup
+    if turns and (K % wl.turns or K < wl.turns):
+        sys.exit(f"--steps must be a positive multiple of the {wl.turns} turns")
     log(f"[bench] workload {wl.name}: {wl.description}")
-    sess = Session(wl, extra_rows=K + W, device=dev)
+    extra = W + (max(0, K // wl.turns - wl.decode_steps) if turns else K)
+    sess = Session(wl, extra_rows=extra, device=dev)
     log(f"[bench] keep per sequence {min(sess.keep)}..{max(sess.keep)}, max_pages "
         f"{sess.max_pages}, blocks {sess.num_blocks}")
 
@@ -205,15 +329,14 @@ def main():
     log(f"[bench] prefill done: {sum(ev_ms):.1f} ms over {sess.n_layers} layers")
 
     # ---- decode inputs and graphs ------------------------------------------
-    inputs = sess.make_inputs(W + K)
+    # multi-turn: W warm-up steps on the prefilled cache, then every turn
+    # (append of the turn's rows, then its steps) inside the timed region
+    n_main = W if turns else W + K
+    inputs = sess.make_inputs(n_main)
     torch.cuda.synchronize()
     graphs = []
     if not args.no_graph:
-        for s in range(W + K):
-            gph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gph):
-                sess.step(inputs[s])
-            graphs.append(gph)
+        graphs = [graph_of(torch, lambda i=i: sess.step(i)) for i in inputs]
         torch.cuda.synchronize()
         log(f"[bench] captured {len(graphs)} step graphs")
 
@@ -227,15 +350,33 @@ def main():
         run(s)
     torch.cuda.synchronize()
     sess.advance(W)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for s in range(W, W + K):
-        run(s)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    sess.advance(K)
+    turn_report = None
+    if turns:
+        spt = K // wl.turns
+        plan = turn_plan(sess, spt)
+        last_inp = plan[-1]["steps"][-1]
+        app_ms, dec_ms, ms_total = run_turns(torch, sess, plan, not args.no_graph)
+        del plan
+        turn_report = {"turns": wl.turns, "steps_per_turn": spt,
+                       "append_rows": wl.turn_append,
+                       "append_ms_per_turn": [round(x, 4) for x in app_ms],
+                       "append_ms_mean": round(sum(app_ms) / len(app_ms), 4),
+                       "decode_ms_per_turn": [round(x, 4) for x in dec_ms],
+                       "decode_us_per_step": round(sum(dec_ms) * 1e3 / K, 3)}
+        log(f"[bench] {wl.turns} turns x ({wl.turn_append}-row append + {spt} steps) in "
+            f"{ms_total:.2f} ms; append {turn_report['append_ms_mean']:.3f} ms per turn, decode "
+            f"{turn_report['decode_us_per_step']:.1f} us per step")
+    else:
+        last_inp = inputs[W + K - 1]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for s in range(W, W + K):
+            run(s)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_total = e0.elapsed_time(e1)
+        sess.advance(K)
     ms_step = ms_total / K
     log(f"[bench] {K} steps in {ms_total:.2f} ms -> {ms_step * 1e3:.1f} us/step")
 
@@ -252,36 +393,41 @@ def main():
     # so the timed region itself gives the average launch duration.  Split-K
     # fused path: the same, per layer the split-K decode_kernel and its merge.
     # Standalone path: the attention launches of every layer, captured alone.
-    per_layer, _, n_new = inputs[W + K - 1]
+    per_layer, _, n_new = last_inp
     mode = rkv.decode_mode(sess.g, sess.B, sess.P, sess.max_pages, wl.k2, wl.k1,
                            rkv.RKV_BF16 if wl.dtype.itemsize == 2 else rkv.RKV_F32)
     if mode in (rkv.RKV_FORM_FUSED, rkv.RKV_FORM_SPLITK):
         kernel = ("decode_kernel" if mode == rkv.RKV_FORM_FUSED
                   else "decode_kernel split-K + attend_merge_kernel")
-        launch_us = ms_total * 1e3 / (K * sess.n_layers)
+        launch_us = (turn_report["decode_us_per_step"] if turns else ms_total * 1e3 / K) \
+            / sess.n_layers
         bytes_launch = step_b / sess.n_layers
     else:
-        kernel = "attend_kernel"
+        kernel = "attend_kernel + attend_merge_kernel"
         for l in range(sess.n_layers):
             rkv.rkv_hsa_select(sess.g, per_layer[l][2], n_new, sess.P, sess.summ[l], wl.k1,
                                wl.k2, sess.page_idx[l], sess.ws)
         torch.cuda.synchronize()
-        gph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gph):
-            for l in range(sess.n_layers):
-                rkv.rkv_hsa_attend(sess.g, per_layer[l][2], sess.caches[l], n_new,
-                                   sess.page_idx[l], wl.k2, sess.scale, sess.out, sess.ws)
+        # back-to-back launches in one graph, so that a replay's own start-up
+        # cost is spread over many launches
+        reps = max(1, 64 // sess.n_layers)
+
+        def attends():
+            for _ in range(reps):
+                for l in range(sess.n_layers):
+                    rkv.rkv_hsa_attend(sess.g, per_layer[l][2], sess.caches[l], n_new,
+                                       sess.page_idx[l], wl.k2, sess.scale, sess.out, sess.ws)
+        gph = graph_of(torch, attends)
         bytes_launch = attend_b0
         gph.replay()
         torch.cuda.synchronize()
-        reps = 20
         k0, k1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         k0.record()
-        for _ in range(reps):
+        for _ in range(4):
             gph.replay()
         k1e.record()
         torch.cuda.synchronize()
-        launch_us = k0.elapsed_time(k1e) * 1e3 / (reps * sess.n_layers)
+        launch_us = k0.elapsed_time(k1e) * 1e3 / (4 * reps * sess.n_layers)
     kern_gbs = bytes_launch / (launch_us * 1e-6) / 1e9
     traffic = counted_traffic(kernel, wl.name, rkv.load_library().rkv_build_id().decode())
     log(f"[bench] {kernel}: {launch_us:.2f} us/launch, {bytes_launch / 1e6:.2f} MB/launch -> "
@@ -317,8 +463,7 @@ def main():
                    "prompt_len_min": min(sess.prompt_lens), "prompt_len_max": max(sess.prompt_lens),
                    "kept_rows_min": min(sess.keep), "kept_rows_max": max(sess.keep),
                    "graph": not args.no_graph,
-                   "path": {rkv.RKV_FORM_STANDALONE: "standalone kernels", rkv.RKV_FORM_FUSED: "fused",
-                            rkv.RKV_FORM_SPLITK: "fused split-K"}[mode],
+                   "path": FORMS[mode],
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(kern_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
@@ -327,6 +472,14 @@ def main():
                      "frac_of_measured_copy": round(kern_gbs / copy_gbs, 4),
                      "bytes_per_launch": int(bytes_launch)},
     }
+    if turn_report:
+        result["config"]["turns"] = wl.turns
+        result["config"]["turn_append_rows"] = wl.turn_append
+        result["turns"] = turn_report
+    if turns and args.mt_filter > 0:
+        del graphs, inputs
+        torch.cuda.empty_cache()
+        result["mt_filter"] = mt_filter_leg(torch, rkv, wl, args, dev, args.mt_filter)
     if not args.no_cpu_baseline:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
         log(f"[bench] timing the oracle on the host ({threads} threads, then 1) ...")

@@ -104,8 +104,9 @@ class Session:
             timer[1].record()
         return k, v, qw
 
-    def append_turn(self, layer: int, turn: int):
-        """Multi-turn workloads: append the turn's rows to every sequence."""
+    def turn_source(self, layer: int, turn: int):
+        """Multi-turn workloads: the turn's rows k, v [B, Hkv, turn_append, d]
+        and the row counts n_old, n_new of the append (device tensors)."""
         n = self.wl.turn_append
         k = torch.zeros((self.B, self.Hkv, n, self.d), dtype=self.wl.dtype, device=self.dev)
         v = torch.zeros_like(k)
@@ -113,10 +114,92 @@ class Session:
             k[b], v[b] = self.wl.turn_rows(self.layer_ids[layer], b, turn, self.positions()[b],
                                            device=self.dev)
         n_old = torch.tensor(self.rows, dtype=torch.int32, device=self.dev)
-        n_new = n_old + n
-        rkv.rkv_append_summaries(self.g, self.caches[layer], n_old, n_new, n, self.summ[layer],
-                                 k_src=k, v_src=v)
-        return k, v
+        return k, v, n_old, n_old + n
+
+    def append_source(self, layer: int, src) -> None:
+        """Enqueues the append of a turn_source result to layer's cache."""
+        k, v, n_old, n_new = src
+        rkv.rkv_append_summaries(self.g, self.caches[layer], n_old, n_new, k.shape[2],
+                                 self.summ[layer], k_src=k, v_src=v)
+
+    def append_turn(self, layer: int, turn: int):
+        """Appends the turn's rows to every sequence of layer (rows are not
+        advanced); returns them."""
+        src = self.turn_source(layer, turn)
+        self.append_source(layer, src)
+        return src[0], src[1]
+
+    # ---- multi-turn view (RocketKV-MT) --------------------------------------
+    def enable_turn_view(self, keep_rows: int, extra_rows: int):
+        """Adds a view cache per layer for the per-turn filter: capacity
+        keep_rows + extra_rows, its own shuffled page table and summaries."""
+        pages = -(-(keep_rows + extra_rows) // self.P)
+        self.view_max_pages = -(-pages // 8) * 8
+        table, nblk = synth.page_table(self.wl.seed + 1, self.B, [pages] * self.B,
+                                       self.view_max_pages)
+        self.view_table = table.to(self.dev)
+        shape = (nblk, self.Hkv, self.P, self.d)
+        self.views, self.view_summ = [], []
+        for _ in range(self.n_layers):
+            self.views.append(rkv.PagedCache(torch.zeros(shape, dtype=self.wl.dtype, device=self.dev),
+                                             torch.zeros(shape, dtype=self.wl.dtype, device=self.dev),
+                                             self.view_table))
+            self.view_summ.append(torch.zeros((self.B, self.Hkv, 2, self.d, self.view_max_pages),
+                                              dtype=self.wl.dtype, device=self.dev))
+        self.view_rows = [0] * self.B
+        self.view_ws = rkv.hsa_workspace(self.g, self.B, self.P, self.view_max_pages, self.wl.k1,
+                                         self.wl.k2, self.dev)
+
+    def turn_window_q(self, layer: int, turn: int):
+        """The turn's last w queries [B, Hq, w, d] (aligned with the turn's
+        needle), at the positions of the turn's last w rows."""
+        wl = self.wl
+        qw = torch.zeros((self.B, self.Hq, wl.window, self.d), dtype=wl.dtype, device=self.dev)
+        for b in range(self.B):
+            qw[b] = wl.turn_window_q(self.layer_ids[layer], b, turn, self.positions()[b],
+                                     device=self.dev)
+        return qw
+
+    def turn_view_keep(self, budget: int):
+        """Rows of every sequence's view: stage 1's share of a total token
+        budget under the adaptive split, at the current history length."""
+        return [rkv.rkv_split_ratio(n / budget, n, self.wl.window)[3] if n > budget else n
+                for n in self.rows]
+
+    def turn_filter_workspace(self):
+        return torch.empty(rkv.rkv_turn_filter_workspace_bytes(self.g, self.B, max(self.rows),
+                                                               self.wl.window),
+                           dtype=torch.uint8, device=self.dev)
+
+    def turn_filter(self, layer: int, qw, keep, ws):
+        """SnapKV++ over the whole retained history of `layer` into its view
+        (enqueue only); keep: rows per sequence."""
+        rkv.rkv_turn_filter(self.g, self.rows, keep, qw, self.wl.window, self.wl.pool_kernel,
+                            self.scale, self.caches[layer], self.views[layer],
+                            view_summaries=self.view_summ[layer], ws=ws)
+
+    def view_step(self, inp):
+        """One decode step on the views (every layer): the token is appended
+        to the full cache and, with HSA, decoded on the view."""
+        per_layer, n_old, n_new, src, view_n = inp
+        for l in range(self.n_layers):
+            k, v, q = per_layer[l]
+            rkv.rkv_append_summaries(self.g, self.caches[l], n_old, n_new, 1, self.summ[l],
+                                     k_src=src[l][0], v_src=src[l][1])
+            rkv.rkv_decode_step(self.g, q, k, v, self.views[l], view_n, self.view_summ[l],
+                                self.wl.k1, self.wl.k2, self.scale, self.out, self.view_ws,
+                                page_idx=self.page_idx[l], opts=self.opts[l])
+
+    def make_view_inputs(self, steps: int, turn: int):
+        """make_inputs plus the per-step row counts of the views and the new
+        rows shaped [B, Hkv, 1, d] for the full cache's append."""
+        base = self.make_inputs(steps, turn=turn)
+        v0 = torch.tensor(self.view_rows, dtype=torch.int32)
+        out = []
+        for s, (per_layer, n_old, n_new) in enumerate(base):
+            src = [(k[:, :, None].contiguous(), v[:, :, None].contiguous()) for k, v, _ in per_layer]
+            out.append((per_layer, n_old, n_new, src, (v0 + s + 1).to(self.dev)))
+        return out
 
     def positions(self):
         """True position of the next token of every sequence."""

@@ -150,6 +150,15 @@ class Workload:
         self._plant(k, layer, list(range(at, at + max(1, self.needle_span))), turn)
         return k.to(self.dtype), v.to(self.dtype)
 
+    def turn_window_q(self, layer: int, seq: int, turn: int, end: int, device="cpu"):
+        """A turn's last w queries [Hq, w, d] at positions end-w .. end-1,
+        aligned with the turn's needle where queries align."""
+        w = self.window
+        q = synth.gaussian_rows(self.seed, (self.name, "turn_qwin", layer, seq, turn),
+                                self.n_q_heads, w, self.head_dim, device=device,
+                                positions=self._pos(end - w, w, device))
+        return self._align(q, layer, turn).to(self.dtype)
+
     def turn_needle_offset(self, layer: int, seq: int, turn: int) -> int:
         """Row offset, within a turn's appended rows, of that turn's needle."""
         g = synth.generator(self.seed, self.name, "turn_needle", layer, seq, turn)
