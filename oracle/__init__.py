@@ -34,22 +34,39 @@ def _src_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _lib_path() -> str:
-    return os.path.join(_HERE, f"liboracle-{_src_hash()}.so")
+def _sanitized() -> bool:
+    """RKV_ORACLE_SANITIZE=1 loads a build under AddressSanitizer and
+    UndefinedBehaviorSanitizer (the process must preload libasan)."""
+    return os.environ.get("RKV_ORACLE_SANITIZE", "") == "1"
 
 
-def build(force: bool = False) -> str:
-    """Compile rkv_oracle.c into a shared library named after its content."""
-    path = _lib_path()
+def _lib_path(sanitize: bool = False) -> str:
+    tag = "liboracle-asan-" if sanitize else "liboracle-"
+    return os.path.join(_HERE, f"{tag}{_src_hash()}.so")
+
+
+def build(force: bool = False, sanitize: bool = False) -> str:
+    """Compile rkv_oracle.c into a shared library named after its content;
+    sanitize=True: with -fsanitize=address,undefined, every UB report fatal."""
+    path = _lib_path(sanitize)
     if force or not os.path.exists(path):
         tmp = path + f".tmp{os.getpid()}"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-fno-builtin", "-Wall", "-o", tmp, _SRC, "-lm"]
+        cmd = ["gcc", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+               "-fno-builtin", "-Wall", "-o", tmp, _SRC, "-lm"]
+        if sanitize:
+            cmd[1:1] = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                        "-fno-sanitize-recover=all"]
+        else:
+            cmd[1:1] = ["-O2"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, path)
+        prefix = "liboracle-asan-" if sanitize else "liboracle-"
         for name in os.listdir(_HERE):
-            if name.startswith("liboracle-") and name.endswith(".so") and \
-                    os.path.join(_HERE, name) != path:
+            if not (name.startswith(prefix) and name.endswith(".so")):
+                continue
+            if not sanitize and name.startswith("liboracle-asan-"):
+                continue
+            if os.path.join(_HERE, name) != path:
                 try:
                     os.remove(os.path.join(_HERE, name))
                 except OSError:
@@ -61,7 +78,7 @@ def _lib():
     global _LIB
     with _LOCK:
         if _LIB is None:
-            lib = ctypes.CDLL(build())
+            lib = ctypes.CDLL(build(sanitize=_sanitized()))
             i64, i32, f32, f64, vp = (ctypes.c_int64, ctypes.c_int, ctypes.c_float,
                                       ctypes.c_double, ctypes.c_void_p)
             P = ctypes.POINTER
