@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 CSV output for the files kept under profiles/.
 
-Two commands:
+Three commands:
 
   stats     kernel time table from a ``--kernel-trace --stats`` run
             (``*_kernel_stats.csv``), restricted to the heaviest kernels.
@@ -9,6 +9,8 @@ Two commands:
             same counter reads for a plain device copy of known size, written
             as JSON together with the library build id, so that a reader can
             tell when the kernel has changed since the counters were taken.
+  pmc       the mean per dispatch of every counter of one or more ``--pmc``
+            runs, over the dispatches of one kernel, as JSON.
 """
 from __future__ import annotations
 
@@ -80,6 +82,23 @@ def counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes, k
     }
 
 
+def pmc_means(paths, kernel):
+    """{counter: mean value per dispatch} over the dispatches whose kernel
+    name contains `kernel`, and the dispatch count of each counter."""
+    sums, counts = {}, {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            c = r["Counter_Name"]
+            sums[c] = sums.get(c, 0.0) + float(r["Counter_Value"])
+            counts[c] = counts.get(c, 0) + 1
+    if not sums:
+        raise SystemExit("no matching dispatches")
+    return ({c: round(sums[c] / counts[c], 3) for c in sorted(sums)},
+            {c: counts[c] for c in sorted(counts)})
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -97,9 +116,22 @@ def main(argv=None):
     c.add_argument("--build-id", required=True)
     c.add_argument("--workload", required=True)
     c.add_argument("--commands", nargs="+", required=True)
+    m = sub.add_parser("pmc")
+    m.add_argument("csv", nargs="+")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--build-id", required=True)
+    m.add_argument("--workload", required=True)
+    m.add_argument("--commands", nargs="+", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.csv, a.top, a.match))
+        return
+    if a.cmd == "pmc":
+        means, counts = pmc_means(a.csv, a.kernel)
+        json.dump({"build_id": a.build_id, "workload": a.workload, "kernel": a.kernel,
+                   "mean_per_dispatch": means, "dispatches": counts, "commands": a.commands},
+                  sys.stdout, indent=1)
+        print()
         return
     res = counters(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes, a.kernel)
     res = {"build_id": a.build_id, "workload": a.workload, **res, "commands": a.commands}

@@ -120,6 +120,7 @@ PATH_OPTS = {
     "splitk": {"form": 3},
     "split": {"form": 1},
     "split-legacy": {"form": 1, "select_radix": 1},
+    "split-chunk64": {"form": 1, "select_chunk": 64},
 }
 
 
@@ -134,7 +135,8 @@ def path(request):
     per unit, the fused kernel split K-wise (plus the merge), or the
     standalone kernels (with several selection chunks: rank-ordered
     candidates and the rank-search merge by default, "split-legacy" the
-    radix top-k and radix merge)."""
+    radix top-k and radix merge, "split-chunk64" 64-page chunks, whose
+    candidates take the radix merge when there are too many lists)."""
     return request.param
 
 
