@@ -118,7 +118,8 @@ typedef struct rkv_paged_cache {
 typedef struct rkv_opts {
     int32_t form;           /* RKV_FORM_*; a form the shapes do not allow falls back to
                                RKV_FORM_STANDALONE */
-    int32_t splitk_blocks;  /* RKV_FORM_SPLITK: blocks to aim for in all (0 = 128) */
+    int32_t splitk_blocks;  /* RKV_FORM_SPLITK: blocks to aim for in all (0 = 128, or 256
+                               when more than 65,536 rows are selected in all) */
     int32_t select_chunk;   /* standalone selection: pages per block (0 = automatic) */
     int32_t select_radix;   /* standalone selection over several chunks: 1 = radix top-k
                                and radix merge instead of rank-ordered lists (0 = auto) */
@@ -378,19 +379,20 @@ int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
  *   k_new, v_new : device [B][Hkv][d], or both NULL (no append: this is then
  *                  rkv_hsa_decode).
  *   summaries    : current for rows [0, n-1) on entry, for [0, n) on return.
- * How it runs (same results every way; G <= 4, G * d <= 512, max_pages <=
- * 2048 and k2 * P <= 2048 are needed for either fused form):
- *   - B * Hkv >= 192 (the batch fills the chip): a single kernel, one
- *     16-wave block per (sequence, KV head);
- *   - smaller batches whose summaries fit the kernel's LDS stage
- *     (max_pages <= 1024 and 2 * k1 * max_pages * sizeof(element) <= 64 KiB,
- *     max_pages rounded up to 16 bytes of elements): the same kernel split
- *     K-wise, about 128 blocks in all, each making the unit's selection and
- *     attending to a share of its pages, then a merge kernel (two launches);
+ * How it runs (same results every way; G <= 4, G * d <= 512 and max_pages
+ * <= 2048 are needed for either fused form):
+ *   - B * Hkv >= 192 (the batch fills the chip) and k2 * P <= 2048: a single
+ *     kernel, one 16-wave block per (sequence, KV head);
+ *   - otherwise, when the summaries fit the kernel's LDS stage (max_pages <=
+ *     1024 and 2 * k1 * max_pages * sizeof(element) <= 64 KiB, max_pages
+ *     rounded up to 16 bytes of elements): the same kernel split K-wise,
+ *     about 128 blocks in all (256 when more than 65,536 rows are selected
+ *     in all, more when a share would exceed 2048 rows),
+ *     each making the unit's selection and attending to a share of its
+ *     pages, then a merge kernel (two launches);
  *   - otherwise the standalone append, select and attention kernels.
- * rkv_opts.form picks a form explicitly: RKV_FORM_FUSED wherever the fused
- * limits hold, RKV_FORM_SPLITK where the stage also fits, else the
- * standalone kernels.
+ * rkv_opts.form picks a form explicitly: RKV_FORM_FUSED wherever its limits
+ * hold, RKV_FORM_SPLITK where the stage fits, else the standalone kernels.
  * Other arguments and errors as for rkv_hsa_decode. */
 /* Which form rkv_decode_step (and rkv_hsa_decode) takes for these shapes and
  * options, by the rule above: RKV_FORM_STANDALONE, RKV_FORM_FUSED or

@@ -36,6 +36,7 @@ constexpr int kFusedMaxPages = 2048;
 constexpr int kFusedMaxRows = 2048;
 constexpr size_t kStageBytes = 64 * 1024;
 constexpr int kSplitBlocks = 128;
+constexpr int kSplitBlocksWide = 256;
 
 constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
 
@@ -337,14 +338,21 @@ bool dispatch_g(int B, int nsp, const rkv_gqa &g, const DecArgs &a, const void *
     return false;
 }
 
-// Split-K shape: about `target` blocks in all (0: kSplitBlocks), whole pages
-// per split.
-void split_counts(int units, int k2, int target, int &n_splits, int &pages_per_split) {
-    if (target <= 0) target = kSplitBlocks;
+// Split-K shape: about `target` blocks in all, whole pages per split, and at
+// most kFusedMaxRows rows per split (a block's row table).  The default
+// target is kSplitBlocks; selections of more than kSplitBlocks * 512 rows
+// in all (a stream that is bandwidth work, not latency) take one block per
+// CU instead.
+void split_counts(int units, int k2, int P, int target, int &n_splits, int &pages_per_split) {
+    if (target <= 0)
+        target = (int64_t)units * k2 * P > (int64_t)kSplitBlocks * 512 ? kSplitBlocksWide
+                                                                       : kSplitBlocks;
     int want = (target + units - 1) / units;
     if (want > k2) want = k2;
     if (want < 1) want = 1;
     pages_per_split = (k2 + want - 1) / want;
+    const int most = kFusedMaxRows / P > 0 ? kFusedMaxRows / P : 1;
+    if (pages_per_split > most) pages_per_split = most;
     n_splits = (k2 + pages_per_split - 1) / pages_per_split;
 }
 
@@ -354,28 +362,33 @@ FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, i
                      const Knobs &kn) {
     FusedPlan p{RKV_FORM_STANDALONE, 0, 0};
     if (g.group * g.head_dim > 512 || g.group > 4) return p;
-    if (max_pages > kFusedMaxPages || (int64_t)k2 * P > kFusedMaxRows) return p;
+    if (max_pages > kFusedMaxPages || P > kFusedMaxRows) return p;
     const int units = B * g.n_kv_heads;
+    // one block per unit holds every selected row in its row table; split-K
+    // blocks hold only their share, so larger selections split further
+    const bool rows_fit = (int64_t)k2 * P <= kFusedMaxRows;
     // split-K needs the staged selection (every page's summaries in LDS),
     // else each of its blocks would read the summaries from memory
     const int esz = dtype == RKV_F32 ? 4 : 2, V = 16 / esz;
     const bool stage_fits = max_pages <= kBlock &&
         (int64_t)2 * k1 * ((max_pages + V - 1) / V * V) * esz <= (int64_t)kStageBytes;
-    int form = units >= 192 ? RKV_FORM_FUSED : (stage_fits ? RKV_FORM_SPLITK : RKV_FORM_STANDALONE);
-    if (kn.form == RKV_FORM_STANDALONE || kn.form == RKV_FORM_FUSED) form = kn.form;
+    int form = units >= 192 && rows_fit ? RKV_FORM_FUSED
+                                        : (stage_fits ? RKV_FORM_SPLITK : RKV_FORM_STANDALONE);
+    if (kn.form == RKV_FORM_STANDALONE) form = RKV_FORM_STANDALONE;
+    else if (kn.form == RKV_FORM_FUSED) form = rows_fit ? RKV_FORM_FUSED : RKV_FORM_STANDALONE;
     else if (kn.form == RKV_FORM_SPLITK) form = stage_fits ? RKV_FORM_SPLITK : RKV_FORM_STANDALONE;
     p.form = form;
     if (form == RKV_FORM_SPLITK)
-        split_counts(units, k2, kn.splitk_blocks, p.n_splits, p.pages_per_split);
+        split_counts(units, k2, P, kn.splitk_blocks, p.n_splits, p.pages_per_split);
     return p;
 }
 
-size_t fused_split_ws_bytes(const rkv_gqa &g, int B, int k2, const Knobs &kn) {
+size_t fused_split_ws_bytes(const rkv_gqa &g, int B, int P, int k2, const Knobs &kn) {
     // the split-K plan's partials for any dtype, k1 and form: the same split
     // count as plan_fused, whatever the batch
     const int units = B * g.n_kv_heads;
     int nsp, pps;
-    split_counts(units, k2, kn.splitk_blocks, nsp, pps);
+    split_counts(units, k2, P, kn.splitk_blocks, nsp, pps);
     return align_up((size_t)units * nsp * g.group * (g.head_dim + 2) * sizeof(float));
 }
 

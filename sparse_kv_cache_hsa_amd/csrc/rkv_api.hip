@@ -69,7 +69,7 @@ HsaWs hsa_ws(const rkv_gqa &g, int B, int P, int max_pages, int k2, const Knobs 
     w.select = align_up(select_ws_bytes(g, B, max_pages, k2, kn));
     w.attend = align_up(attend_ws_bytes(g, B, P, k2, kn));
     w.pages = align_up((size_t)B * g.n_kv_heads * k2 * sizeof(int32_t));
-    w.split = fused_split_ws_bytes(g, B, k2, kn);
+    w.split = fused_split_ws_bytes(g, B, P, k2, kn);
     // +256 so that the size is never 0
     w.total = w.select + w.attend + w.pages + w.split + 256;
     return w;

@@ -392,7 +392,7 @@ struct FusedPlan {
 };
 FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, int k1, int k2,
                      const Knobs &kn);
-size_t fused_split_ws_bytes(const rkv_gqa &g, int B, int k2, const Knobs &kn);
+size_t fused_split_ws_bytes(const rkv_gqa &g, int B, int P, int k2, const Knobs &kn);
 int launch_decode_fused(const FusedPlan &pl, const rkv_gqa &g, int dtype, int B, const void *q,
                         const void *k_new, const void *v_new, const rkv_paged_cache &c,
                         const int32_t *seq_lens, void *summaries, int k1, int k2, float scale,

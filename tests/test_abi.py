@@ -175,12 +175,17 @@ def test_decode_mode_rule(rkv_lib):
     assert L.decode_mode(g, 1, 16, 600, 32, 32) == S       # stage too small for 600 pages
     assert L.decode_mode(L.gqa(2, 8, 128), 1, 16, 64, 16, 16) == S   # G > 4
     assert L.decode_mode(L.gqa(2, 4, 64), 1, 16, 130, 16, 16, L.RKV_F32) == K
+    # a selection of more rows than one block's table (128 pages x 32 rows):
+    # split-K, each share within the table
+    assert L.decode_mode(g, 4, 32, 208, 128, 32) == K
+    assert L.decode_mode(g, 32, 32, 208, 128, 32) == K
     o = L.make_opts
     assert L.decode_mode(g, 32, 16, 400, 64, 32, opts=o(form=S)) == S
     assert L.decode_mode(g, 32, 16, 400, 64, 32, opts=o(form=K)) == K
     assert L.decode_mode(g, 1, 16, 600, 32, 32, opts=o(form=K)) == S   # not past the stage
     assert L.decode_mode(g, 1, 16, 216, 32, 32, opts=o(form=F)) == F
     assert L.decode_mode(g, 4, 32, 4400, 128, 32, opts=o(form=F)) == S  # not past the limits
+    assert L.decode_mode(g, 4, 32, 208, 128, 32, opts=o(form=F)) == S   # rows beyond one block
     assert L.decode_mode(g, 1, 16, 216, 32, 32, opts=o(form=L.RKV_FORM_AUTO)) == K
     lib = L.load_library()
     assert lib.rkv_decode_mode(ctypes.byref(g), 1, 0, 16, 100, 8, 8, None) == L.RKV_EINVAL

@@ -42,6 +42,9 @@ DECODE_CASES = [
     # k2 in (128, 256] over several selection chunks: the rank-ordered
     # candidate merge with four keys per lane
     (BF16, 1, 2, 4, 128, 8, 32, 200, [4000], 600),
+    # a RocketKV-MT view's shape: 128 pages of 32 rows selected, more rows
+    # than one block's table, so split-K shares of at most 2,048 rows
+    (BF16, 2, 8, 4, 128, 32, 32, 128, [6500, 5001], 208),
 ]
 
 
