@@ -62,7 +62,7 @@ extern "C" {
 
 /* Supported shapes: head_dim in {64, 128}; group in {1, 2, 4, 8};
  * page_size in [1, 256]; 1 <= k1 <= head_dim; 1 <= k2 <= RKV_MAX_K2. */
-#define RKV_MAX_K2 1024
+#define RKV_MAX_K2 4096
 #define RKV_MAX_EVICT_BATCH 128
 
 /* GQA layout: Hq = n_kv_heads * group query heads. */

@@ -83,7 +83,8 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     constexpr bool kPacked = std::is_same<T, uint16_t>::value;
     __shared__ int ch_s[D];
     __shared__ T ovr_hi[D], ovr_lo[D], xs[D];
-    __shared__ int32_t sel_s[RKV_MAX_K2];
+    // the selected pages: K = min(k2, NP) <= max_pages <= kFusedMaxPages
+    __shared__ int32_t sel_s[kFusedMaxPages];
     __shared__ int32_t blk_s[kFusedMaxPages];
     __shared__ int cnt_s[kBlock];
     __shared__ uint32_t pkey_s[kBlock];  // page score keys of the staged path's top-k

@@ -48,8 +48,9 @@ def measure(wl: workloads.Workload, steps: int, device="cuda") -> dict:
     sess.prefill_layer(0)
     B, Hkv, G, d, P = sess.B, sess.Hkv, sess.G, sess.d, sess.P
     budget = wl.k2 * P
-    if budget > 1024:
-        raise SystemExit(f"token budget {budget} exceeds the library's k2 limit of 1024")
+    if budget > rkv.RKV_MAX_K2:
+        raise SystemExit(f"token budget {budget} exceeds the library's k2 limit of "
+                         f"{rkv.RKV_MAX_K2}")
     g = sess.g
     # page-1 copy of the same logical rows (identity page table)
     cap = max(sess.capacity)

@@ -28,7 +28,7 @@ RKV_ESCRATCH = -6
 RKV_STATIC_SCRATCH_BYTES = 16 << 20
 RKV_F32 = 0
 RKV_BF16 = 1
-RKV_MAX_K2 = 1024
+RKV_MAX_K2 = 4096
 RKV_MAX_EVICT_BATCH = 128
 RKV_FORM_AUTO = 0
 RKV_FORM_STANDALONE = 1

@@ -45,6 +45,9 @@ DECODE_CASES = [
     # a RocketKV-MT view's shape: 128 pages of 32 rows selected, more rows
     # than one block's table, so split-K shares of at most 2,048 rows
     (BF16, 2, 8, 4, 128, 32, 32, 128, [6500, 5001], 208),
+    # token-level selection (page 1) with k2 above 1,024, up to the limit
+    (BF16, 1, 2, 4, 128, 1, 32, 2000, [5000], 5100),
+    (F32, 1, 1, 2, 64, 1, 8, 4096, [4500], 4600),
 ]
 
 
