@@ -379,12 +379,14 @@ int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
  *   k_new, v_new : device [B][Hkv][d], or both NULL (no append: this is then
  *                  rkv_hsa_decode).
  *   summaries    : current for rows [0, n-1) on entry, for [0, n) on return.
- * How it runs (same results every way; G <= 4, G * d <= 512 and max_pages
- * <= 2048 are needed for either fused form):
+ * How it runs (same results every way; max_pages <= 2048 is needed for
+ * either fused form; groups of 8 run 8-wave blocks, whose split-K stage
+ * holds at most 512 pages):
  *   - B * Hkv >= 192 (the batch fills the chip) and k2 * P <= 2048: a single
  *     kernel, one 16-wave block per (sequence, KV head);
  *   - otherwise, when the summaries fit the kernel's LDS stage (max_pages <=
- *     1024 and 2 * k1 * max_pages * sizeof(element) <= 64 KiB, max_pages
+ *     1024, 512 for G = 8, and 2 * k1 * max_pages * sizeof(element) <= 64 KiB,
+ *     max_pages
  *     rounded up to 16 bytes of elements): the same kernel split K-wise,
  *     about 128 blocks in all (256 when more than 65,536 rows are selected
  *     in all, more when a share would exceed 2048 rows),

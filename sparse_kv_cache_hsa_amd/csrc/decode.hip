@@ -5,7 +5,8 @@
 // The steps are those of RocketKV's decode path ("RocketKV-adapted --
 // Two-Stage Compression": "Where it sits" for the two-dimensional score bound,
 // "Adaptation notes" for whole-page selection, "Evidence" for the incremental
-// summary update).  One block of 16 waves owns one (sequence, KV head): the
+// summary update).  One block of 16 waves (8 for groups of 8 query heads)
+// owns one (sequence, KV head): the
 // chosen channels, page scores and page list never leave LDS, and the block's
 // attention phase starts as soon as its own selection is done, so a layer
 // costs one launch and one dependent chain of memory round trips instead of
@@ -31,7 +32,7 @@ namespace rkv {
 namespace {
 
 constexpr int kNW = 16;
-constexpr int kBlock = kNW * kWave;
+constexpr int fused_waves(int G) { return G > 4 ? 8 : kNW; }
 constexpr int kFusedMaxPages = 2048;
 constexpr int kFusedMaxRows = 2048;
 constexpr size_t kStageBytes = 64 * 1024;
@@ -69,11 +70,14 @@ struct DecArgs {
     } while (0)
 #endif
 
-template <typename T, int D, int G, bool SPLIT>
-__global__ void __launch_bounds__(kBlock)
+// NW waves per block: 16, or 8 for groups of 8 query heads (their attention
+// state needs twice the registers and LDS per wave).
+template <typename T, int D, int G, bool SPLIT, int NW>
+__global__ void __launch_bounds__(NW *kWave)
 decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, T *v_pool,
               T *summ) {
-    using Core = AttendCore<T, D, G, kNW, 2, false>;
+    constexpr int kBlock = NW * kWave;
+    using Core = AttendCore<T, D, G, NW, 2, false>;
     constexpr size_t kKeyBytes = sizeof(uint64_t) * kFusedMaxPages;
     constexpr size_t kRowBytes = sizeof(uint32_t) * kFusedMaxRows;
     constexpr size_t kUnion = cmax(cmax(kStageBytes, kKeyBytes), kRowBytes);
@@ -89,7 +93,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     __shared__ int cnt_s[kBlock];
     __shared__ uint32_t pkey_s[kBlock];  // page score keys of the staged path's top-k
     __shared__ uint32_t hist[256];
-    __shared__ int wave_tot[kNW];
+    __shared__ int wave_tot[NW];
     __shared__ int sh[2];
     // staged summaries or page keys (selection), then the row table
     // (attention): never live at the same time
@@ -317,12 +321,13 @@ template <typename T, int D, int G>
 void launch_t(int B, int nsp, const rkv_gqa &g, const DecArgs &a, const void *q,
               const void *k_new, const void *v_new, const rkv_paged_cache &c, void *summ,
               hipStream_t s) {
+    constexpr int NW = fused_waves(G);
     if (nsp > 0)
-        decode_kernel<T, D, G, true><<<dim3(nsp, g.n_kv_heads, B), kBlock, 0, s>>>(
+        decode_kernel<T, D, G, true, NW><<<dim3(nsp, g.n_kv_heads, B), NW * kWave, 0, s>>>(
             a, (const T *)q, (const T *)k_new, (const T *)v_new, (T *)c.k_pool, (T *)c.v_pool,
             (T *)summ);
     else
-        decode_kernel<T, D, G, false><<<dim3(g.n_kv_heads, B), kBlock, 0, s>>>(
+        decode_kernel<T, D, G, false, NW><<<dim3(g.n_kv_heads, B), NW * kWave, 0, s>>>(
             a, (const T *)q, (const T *)k_new, (const T *)v_new, (T *)c.k_pool, (T *)c.v_pool,
             (T *)summ);
 }
@@ -335,6 +340,7 @@ bool dispatch_g(int B, int nsp, const rkv_gqa &g, const DecArgs &a, const void *
         case 1: launch_t<T, D, 1>(B, nsp, g, a, q, k_new, v_new, c, summ, s); return true;
         case 2: launch_t<T, D, 2>(B, nsp, g, a, q, k_new, v_new, c, summ, s); return true;
         case 4: launch_t<T, D, 4>(B, nsp, g, a, q, k_new, v_new, c, summ, s); return true;
+        case 8: launch_t<T, D, 8>(B, nsp, g, a, q, k_new, v_new, c, summ, s); return true;
     }
     return false;
 }
@@ -362,7 +368,8 @@ void split_counts(int units, int k2, int P, int target, int &n_splits, int &page
 FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, int k1, int k2,
                      const Knobs &kn) {
     FusedPlan p{RKV_FORM_STANDALONE, 0, 0};
-    if (g.group * g.head_dim > 512 || g.group > 4) return p;
+    if (g.group > 8) return p;
+    const int block = fused_waves(g.group) * kWave;
     if (max_pages > kFusedMaxPages || P > kFusedMaxRows) return p;
     const int units = B * g.n_kv_heads;
     // one block per unit holds every selected row in its row table; split-K
@@ -371,7 +378,7 @@ FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, i
     // split-K needs the staged selection (every page's summaries in LDS),
     // else each of its blocks would read the summaries from memory
     const int esz = dtype == RKV_F32 ? 4 : 2, V = 16 / esz;
-    const bool stage_fits = max_pages <= kBlock &&
+    const bool stage_fits = max_pages <= block &&
         (int64_t)2 * k1 * ((max_pages + V - 1) / V * V) * esz <= (int64_t)kStageBytes;
     int form = units >= 192 && rows_fit ? RKV_FORM_FUSED
                                         : (stage_fits ? RKV_FORM_SPLITK : RKV_FORM_STANDALONE);

@@ -173,7 +173,9 @@ def test_decode_mode_rule(rkv_lib):
     assert L.decode_mode(g, 1, 16, 216, 32, 32) == K       # batch 1: split-K
     assert L.decode_mode(g, 4, 32, 4400, 128, 32) == S     # beyond the fused page limit
     assert L.decode_mode(g, 1, 16, 600, 32, 32) == S       # stage too small for 600 pages
-    assert L.decode_mode(L.gqa(2, 8, 128), 1, 16, 64, 16, 16) == S   # G > 4
+    assert L.decode_mode(L.gqa(2, 8, 128), 1, 16, 64, 16, 16) == K   # G = 8: 8-wave blocks
+    assert L.decode_mode(L.gqa(2, 8, 128), 1, 16, 600, 16, 16) == S  # their stage: 512 pages
+    assert L.decode_mode(L.gqa(32, 8, 128), 8, 16, 400, 64, 32) == F
     assert L.decode_mode(L.gqa(2, 4, 64), 1, 16, 130, 16, 16, L.RKV_F32) == K
     # a selection of more rows than one block's table (128 pages x 32 rows):
     # split-K, each share within the table

@@ -45,6 +45,9 @@ DECODE_CASES = [
     # a RocketKV-MT view's shape: 128 pages of 32 rows selected, more rows
     # than one block's table, so split-K shares of at most 2,048 rows
     (BF16, 2, 8, 4, 128, 32, 32, 128, [6500, 5001], 208),
+    # groups of 8 query heads: 8-wave fused blocks, one per unit at 192 units
+    (BF16, 24, 8, 8, 128, 16, 32, 64, [1000 + 41 * i for i in range(24)], 128),
+    (F32, 24, 8, 8, 64, 16, 16, 32, [800 + 13 * i for i in range(24)], 72),
     # token-level selection (page 1) with k2 above 1,024, up to the limit
     (BF16, 1, 2, 4, 128, 1, 32, 2000, [5000], 5100),
     (F32, 1, 1, 2, 64, 1, 8, 4096, [4500], 4600),
@@ -156,7 +159,7 @@ def case_mode(case, opts=None):
 
 def fused_supported(case):
     dtype, B, Hkv, G, d, P, k1, k2, lens, max_pages = case
-    return G <= 4 and G * d <= 512 and max_pages <= 2048 and k2 * P <= 2048
+    return G <= 8 and max_pages <= 2048 and k2 * P <= 2048
 
 
 @pytest.mark.parametrize("ci", range(len(DECODE_CASES)))
