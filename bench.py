@@ -313,9 +313,9 @@ def mt_filter_leg(torch, rkv, wl, args, dev, budget: int):
     most = max(rkv.rkv_split_ratio(n / budget, n, wl.window)[3] if n > budget else n
                for n in final)
     sess.enable_turn_view(most, spt + 1)
-    sess.rows = [n + wl.turns * wl.turn_append + (wl.turns - 1) * spt for n in sess.rows]
-    ws = sess.turn_filter_workspace()
-    sess.rows = [n - wl.turns * wl.turn_append - (wl.turns - 1) * spt for n in sess.rows]
+    # the last turn's filter sees the longest history
+    ws = sess.turn_filter_workspace(max(sess.rows) + wl.turns * wl.turn_append
+                                    + (wl.turns - 1) * spt)
     plan = turn_plan(sess, spt, view_budget=budget)
     torch.cuda.synchronize()
     pro, dec, total = run_turns(torch, sess, plan, not args.no_graph, view_ws=ws)

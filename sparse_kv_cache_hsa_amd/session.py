@@ -166,8 +166,11 @@ class Session:
         return [rkv.rkv_split_ratio(n / budget, n, self.wl.window)[3] if n > budget else n
                 for n in self.rows]
 
-    def turn_filter_workspace(self):
-        return torch.empty(rkv.rkv_turn_filter_workspace_bytes(self.g, self.B, max(self.rows),
+    def turn_filter_workspace(self, max_rows: int | None = None):
+        """Workspace of turn_filter for histories of up to max_rows rows
+        (default: the current ones)."""
+        L_max = max(self.rows) if max_rows is None else max_rows
+        return torch.empty(rkv.rkv_turn_filter_workspace_bytes(self.g, self.B, L_max,
                                                                self.wl.window),
                            dtype=torch.uint8, device=self.dev)
 
