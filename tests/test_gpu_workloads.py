@@ -43,7 +43,13 @@ _POOL = cf.ThreadPoolExecutor(THREADS)
 
 
 def say(*a):
+    """Progress: printed, and appended to gpurun_out/parity/progress.log so
+    that a run whose output pytest captures still shows it is alive."""
     print(*a, flush=True)
+    d = os.path.join(ROOT, "gpurun_out", "parity")
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "progress.log"), "a") as f:
+        print(*a, file=f, flush=True)
 
 
 def pmap(fn, items):
@@ -202,7 +208,7 @@ def decode_and_check(sess, ounits, steps, when=None, turn=0, stats=None, needle=
                     stats["needle_page_hits"] = stats.get("needle_page_hits", 0) + int(hit)
                     stats["needle_page_checks"] = stats.get("needle_page_checks", 0) + 1
             checked += 1
-        if s % 16 == 0:
+        if s % 4 == 0:
             say(f"  step {s}: checks so far {checked}")
     sess.advance(steps)
     torch.cuda.synchronize()
