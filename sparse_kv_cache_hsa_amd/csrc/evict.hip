@@ -507,6 +507,71 @@ gather_kernel(int Hkv, int64_t L_max, EvictSeq seq, const int32_t *kept, int64_t
     ((uint4 *)(v_pool + dst))[chunk] = ((const uint4 *)(v + src))[chunk];
 }
 
+// The gather and the summary rebuild in one pass, one block per destination
+// page: the page's kept rows are copied into the cache with 16-byte chunks,
+// their K rows staged in LDS ([row][D], dynamic), then one thread per
+// channel scans them in ascending row order with strict comparisons (the
+// first of equal values kept) -- the same scan as the rebuild of
+// append_kernel, without reading the rows back from the pool.  A kept index
+// outside the prompt leaves that cache row as it was and stages its current
+// contents.  Used when a page's rows fit kGatherSummBytes of LDS.
+constexpr size_t kGatherSummBytes = 32 * 1024;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+gather_summ_kernel(int Hkv, int64_t L_max, EvictSeq seq, const int32_t *kept,
+                   int64_t kept_stride, const T *k, const T *v, T *k_pool, T *v_pool,
+                   const int32_t *page_table, int P, int max_pages, int64_t num_blocks, T *summ,
+                   int32_t *status) {
+    extern __shared__ __align__(16) unsigned char gs_raw[];
+    T *rows_s = (T *)gs_raw;                       // [P][D]
+    constexpr int V = 16 / (int)sizeof(T);         // elements per 16-byte chunk
+    constexpr int CPR = D / V;                      // chunks per row
+    const int b = blockIdx.z, h = blockIdx.y, tid = threadIdx.x;
+    const int64_t L = seq.L[b];
+    const int64_t keep_eff = min<int64_t>(seq.keep[b], L);
+    const int64_t pg = blockIdx.x;
+    const int64_t r0 = pg * P;
+    if (r0 >= keep_eff) return;
+    const int nrows = (int)min<int64_t>(P, keep_eff - r0);
+    const int32_t blk = page_table[(int64_t)b * max_pages + pg];
+    if (blk < 0 || blk >= num_blocks) {
+        if (tid == 0) report(status, RKV_DEV_BLOCK);
+        return;
+    }
+    const int64_t bh = (int64_t)b * Hkv + h;
+    T *kp = k_pool + ((int64_t)blk * Hkv + h) * P * D;
+    T *vp = v_pool + ((int64_t)blk * Hkv + h) * P * D;
+    for (int i = tid; i < nrows * CPR; i += 256) {
+        const int row = i / CPR, chunk = i - row * CPR;
+        const int32_t t = kept[bh * kept_stride + r0 + row];
+        uint4 kx;
+        if (t >= 0 && t < L) {
+            const int64_t src = (bh * L_max + t) * D;
+            kx = ((const uint4 *)(k + src))[chunk];
+            ((uint4 *)(kp + (int64_t)row * D))[chunk] = kx;
+            ((uint4 *)(vp + (int64_t)row * D))[chunk] = ((const uint4 *)(v + src))[chunk];
+        } else {
+            kx = ((const uint4 *)(kp + (int64_t)row * D))[chunk];
+        }
+        ((uint4 *)(rows_s + (int64_t)row * D))[chunk] = kx;
+    }
+    __syncthreads();
+    for (int c = tid; c < D; c += 256) {
+        T bmax = rows_s[c], bmin = rows_s[c];
+        float fmax_ = Elem<T>::ld(&bmax, 0), fmin_ = fmax_;
+        for (int r = 1; r < nrows; ++r) {
+            const T x = rows_s[(int64_t)r * D + c];
+            const float fx = Elem<T>::ld(&x, 0);
+            if (fx > fmax_) { fmax_ = fx; bmax = x; }
+            if (fx < fmin_) { fmin_ = fx; bmin = x; }
+        }
+        T *sm = summ + bh * 2 * D * max_pages;
+        sm[(int64_t)c * max_pages + pg] = bmax;
+        sm[(int64_t)(D + c) * max_pages + pg] = bmin;
+    }
+}
+
 template <typename T, int D>
 int launch_t(const rkv_gqa &g, int B, const EvictSeq &seq, int64_t L_max, int w, int pool_kernel,
              float scale, const void *q_win, const void *k, const void *v,
@@ -553,6 +618,16 @@ int launch_t(const rkv_gqa &g, int B, const EvictSeq &seq, int64_t L_max, int w,
     maxpool_kernel<<<dim3(blocks_t, Hkv, B), 256, 0, s>>>(Hkv, w, L_max, seq, pool_kernel / 2, A, pl);
     keep_kernel<<<dim3(Hkv, B), kKeepBlock, 0, s>>>(Hkv, w, L_max, seq, pl, kept, kstride, nold,
                                                     nnew, seq_lens_out);
+    const size_t page_bytes = (size_t)c.page_size * D * sizeof(T);
+    const bool fused_summ = summaries && page_bytes <= kGatherSummBytes;
+    if (keep_rows > 0 && fused_summ) {
+        const int pages = (int)((keep_rows + c.page_size - 1) / c.page_size);
+        gather_summ_kernel<T, D><<<dim3(pages, Hkv, B), 256, page_bytes, s>>>(
+            Hkv, L_max, seq, kept, kstride, (const T *)k, (const T *)v, (T *)c.k_pool,
+            (T *)c.v_pool, c.page_table, c.page_size, c.max_pages, c.num_blocks,
+            (T *)summaries, status);
+        return launch_status();
+    }
     if (keep_rows > 0) {
         constexpr int RPB = 256 / (D * (int)sizeof(T) / 16);
         gather_kernel<T, D><<<dim3((int)((keep_rows + RPB - 1) / RPB), Hkv, B), 256, 0, s>>>(
