@@ -107,75 +107,75 @@ logits_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, const T *q_win
     }
 }
 
-// Register-tiled logits for 16-byte aligned inputs.  A block covers 128
-// window rows (row group blockIdx.x / ntiles) against 64 keys (tile
-// blockIdx.x % ntiles); each of its 256 threads computes 4 rows x 8 keys.
-// Channels are staged through LDS 32 at a time (channel-major, fp32), and
-// every dot product still runs over the channels in ascending order, one
-// rounding per step, exactly as in logits_kernel -- only the number of LDS
-// reads per multiply-add drops (3 vector reads per 32 of them instead of 8).
+// Register-tiled logits for 16-byte aligned inputs, 8 rows x 8 keys per
+// thread: a block covers 128 window rows against 128 keys (two of the 64-key tiles whose maxima TM
+// holds).  Every dot product still runs over the channels in ascending
+// order, one rounding per step, as in logits_kernel; each channel step reads
+// four 16-byte LDS vectors for 64 multiply-adds.
 constexpr int kLtRows = 128, kLtKeys = 64, kLtChunk = 32;
+constexpr int kL2Keys = 128;
 
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 logits_tiled_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, const T *q_win,
-                    const T *k, float scale, int ntiles, float *Z, float *TM) {
-    constexpr int V = Vec16<T>::N;            // elements per 16-byte load
-    constexpr int VPR = kLtChunk / V;         // 16-byte loads per row and chunk
+                     const T *k, float scale, int ntiles, int ntiles2, float *Z, float *TM) {
+    constexpr int V = Vec16<T>::N;
+    constexpr int VPR = kLtChunk / V;
     __shared__ __align__(16) float qs[kLtChunk][kLtRows];
-    __shared__ __align__(16) float ks[kLtChunk][kLtKeys];
-    __shared__ float tm_s[kLtKeys / 8][kLtRows];
+    __shared__ __align__(16) float ks[kLtChunk][kL2Keys];
+    __shared__ float tm_s[kL2Keys / 8][kLtRows];
     const int b = blockIdx.z, h = blockIdx.y, tid = threadIdx.x;
-    const int tile = blockIdx.x % ntiles, r0 = (blockIdx.x / ntiles) * kLtRows;
+    const int tile2 = blockIdx.x % ntiles2, r0 = (blockIdx.x / ntiles2) * kLtRows;
     const int64_t L = seq.L[b];
     if (seq.keep[b] >= L) return;
-    const int64_t t0 = (int64_t)tile * kLtKeys;
+    const int64_t t0 = (int64_t)tile2 * kL2Keys;
     if (t0 >= L) return;
     const int64_t bh = (int64_t)b * Hkv + h;
-    const int nk = (int)min<int64_t>(kLtKeys, L - t0);
-    const int rt = tid & 31, kt = tid >> 5;   // rows rt*4.., keys kt*8..
+    const int nk = (int)min<int64_t>(kL2Keys, L - t0);
+    const int rt = tid & 15, kt = tid >> 4;   // rows rt*8.., keys kt*8..
     const T *qb = q_win + (bh * R) * D;
     const T *kb = k + (bh * L_max + t0) * D;
-    float acc[4][8];
+    float acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
     for (int c0 = 0; c0 < D; c0 += kLtChunk) {
         for (int i = tid; i < kLtRows * VPR; i += 256) {
-            const int r = i / VPR, v = i % VPR;
+            const int r = i / VPR, vv = i % VPR;
             float x[V];
             if (r0 + r < R) {
-                Vec16<T>::unpack(*(const uint4 *)(qb + (int64_t)(r0 + r) * D + c0 + v * V), x);
+                Vec16<T>::unpack(*(const uint4 *)(qb + (int64_t)(r0 + r) * D + c0 + vv * V), x);
             } else {
 #pragma unroll
                 for (int e = 0; e < V; ++e) x[e] = 0.0f;
             }
 #pragma unroll
-            for (int e = 0; e < V; ++e) qs[v * V + e][r] = x[e];
+            for (int e = 0; e < V; ++e) qs[vv * V + e][r] = x[e];
         }
-        for (int i = tid; i < kLtKeys * VPR; i += 256) {
-            const int t = i / VPR, v = i % VPR;
+        for (int i = tid; i < kL2Keys * VPR; i += 256) {
+            const int t = i / VPR, vv = i % VPR;
             float x[V];
             if (t < nk) {
-                Vec16<T>::unpack(*(const uint4 *)(kb + (int64_t)t * D + c0 + v * V), x);
+                Vec16<T>::unpack(*(const uint4 *)(kb + (int64_t)t * D + c0 + vv * V), x);
             } else {
 #pragma unroll
                 for (int e = 0; e < V; ++e) x[e] = 0.0f;
             }
 #pragma unroll
-            for (int e = 0; e < V; ++e) ks[v * V + e][t] = x[e];
+            for (int e = 0; e < V; ++e) ks[vv * V + e][t] = x[e];
         }
         __syncthreads();
-#pragma unroll 4
+#pragma unroll 2
         for (int c = 0; c < kLtChunk; ++c) {
-            const float4 qv = *(const float4 *)&qs[c][rt * 4];
+            const float4 qa = *(const float4 *)&qs[c][rt * 8];
+            const float4 qc = *(const float4 *)&qs[c][rt * 8 + 4];
             const float4 ka = *(const float4 *)&ks[c][kt * 8];
             const float4 kc = *(const float4 *)&ks[c][kt * 8 + 4];
-            const float qq[4] = {qv.x, qv.y, qv.z, qv.w};
+            const float qq[8] = {qa.x, qa.y, qa.z, qa.w, qc.x, qc.y, qc.z, qc.w};
             const float kk[8] = {ka.x, ka.y, ka.z, ka.w, kc.x, kc.y, kc.z, kc.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     if constexpr (sizeof(T) == 2)
@@ -186,41 +186,43 @@ logits_tiled_kernel(int Hkv, int R, int w, int64_t L_max, EvictSeq seq, const T 
         }
         __syncthreads();
     }
-    float tmax[4];
+    float tmax[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tmax[i] = -INFINITY;
+    for (int i = 0; i < 8; ++i) tmax[i] = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int tt = kt * 8 + j;
         if (tt >= nk) break;
-        float z[4];
+        float z[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             z[i] = acc[i][j] * scale;
-            const int r = r0 + rt * 4 + i;
+            const int r = r0 + rt * 8 + i;
             const int64_t last = L - w + (r % w);
             if (r < R && t0 + tt <= last) tmax[i] = fmaxf(tmax[i], z[i]);
         }
-        float *zr = Z + (bh * L_max + t0 + tt) * R + r0 + rt * 4;
-        if (r0 + rt * 4 + 3 < R && ((R & 3) == 0)) {
-            // the logits are streamed: written once here, read once by each
-            // of the two later passes (non-temporal hint on all three)
+        float *zr = Z + (bh * L_max + t0 + tt) * R + r0 + rt * 8;
+        if (r0 + rt * 8 + 7 < R && ((R & 3) == 0)) {
             typedef float f32x4 __attribute__((ext_vector_type(4)));
             __builtin_nontemporal_store(f32x4{z[0], z[1], z[2], z[3]}, (f32x4 *)zr);
+            __builtin_nontemporal_store(f32x4{z[4], z[5], z[6], z[7]}, (f32x4 *)(zr + 4));
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (r0 + rt * 4 + i < R) zr[i] = z[i];
+            for (int i = 0; i < 8; ++i)
+                if (r0 + rt * 8 + i < R) zr[i] = z[i];
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tm_s[kt][rt * 4 + i] = tmax[i];
+    for (int i = 0; i < 8; ++i) tm_s[kt][rt * 8 + i] = tmax[i];
     __syncthreads();
-    if (tid < kLtRows && r0 + tid < R) {
-        float m = tm_s[0][tid];
+    // the maxima of the two 64-key tiles this block covers
+    const int half = tid / kLtRows, row = tid % kLtRows;
+    const int tile = tile2 * 2 + half;
+    if (r0 + row < R && tile < ntiles && t0 + (int64_t)half * kLtKeys < L) {
+        float m = tm_s[half * 8][row];
 #pragma unroll
-        for (int q = 1; q < kLtKeys / 8; ++q) m = fmaxf(m, tm_s[q][tid]);
-        TM[(bh * ntiles + tile) * R + r0 + tid] = m;
+        for (int q = 1; q < 8; ++q) m = fmaxf(m, tm_s[half * 8 + q][row]);
+        TM[(bh * ntiles + tile) * R + r0 + row] = m;
     }
 }
 
@@ -597,8 +599,9 @@ int launch_t(const rkv_gqa &g, int B, const EvictSeq &seq, int64_t L_max, int w,
 
     if (((uintptr_t)q_win & 15u) == 0 && ((uintptr_t)Z & 15u) == 0) {
         const int rgroups = (R + kLtRows - 1) / kLtRows;
-        logits_tiled_kernel<T, D><<<dim3(l.ntiles * rgroups, Hkv, B), 256, 0, s>>>(
-            Hkv, R, w, L_max, seq, (const T *)q_win, (const T *)k, scale, l.ntiles, Z, TM);
+        const int ntiles2 = (int)((L_max + kL2Keys - 1) / kL2Keys);
+        logits_tiled_kernel<T, D><<<dim3(ntiles2 * rgroups, Hkv, B), 256, 0, s>>>(
+            Hkv, R, w, L_max, seq, (const T *)q_win, (const T *)k, scale, l.ntiles, ntiles2, Z, TM);
     } else {
         logits_kernel<T, D><<<dim3(l.ntiles, Hkv, B), kLogitsBlock, 0, s>>>(
             Hkv, R, w, L_max, seq, (const T *)q_win, (const T *)k, scale, l.ntiles, Z, TM);
