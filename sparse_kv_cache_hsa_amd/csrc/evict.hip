@@ -401,6 +401,11 @@ colsum_tiled_kernel(int Hkv, int G, int w, int64_t L_max, EvictSeq seq, const fl
         constexpr int kBatch = 8;
         const int r = tid % R;
         const float mr = Ms[r], er = Es[r];
+        // x / er as x * (1/er) plus one residual correction: with 1/er
+        // correctly rounded (an IEEE division, once per row), the corrected
+        // quotient is the correctly rounded x / er for results in the normal
+        // range (Markstein's theorem on division by reciprocal and FMA)
+        const float inv = 1.0f / er;
         for (int tb = tid / R; tb < nk; tb += per * kBatch) {
             float z[kBatch];
 #pragma unroll
@@ -411,7 +416,12 @@ colsum_tiled_kernel(int Hkv, int G, int w, int64_t L_max, EvictSeq seq, const fl
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const int tt = tb + u * per;
-                if (tt < nk) ps[tt * RS + r] = expf(z[u] - mr) / er;
+                if (tt < nk) {
+                    const float x = expf(z[u] - mr);
+                    const float q0 = x * inv;
+                    const float rr = __builtin_fmaf(-q0, er, x);
+                    ps[tt * RS + r] = __builtin_fmaf(rr, inv, q0);
+                }
             }
         }
     }
