@@ -8,8 +8,10 @@
 // widened exactly).
 //
 // Layout of the work inside a block of NW waves:
-//   - the block's rows are listed in an LDS table (row_s) of row units
-//     (block * Hkv + h) * P + slot, or kBadRow for rows that do not exist;
+//   - the block's rows are given as row units (block * Hkv + h) * P + slot,
+//     or kBadRow for rows that do not exist: listed in an LDS table (row_s),
+//     or resolved by the caller's function one iteration ahead of the
+//     loads that use them;
 //   - a row of d elements is read by LPR lanes with one 16-byte non-temporal
 //     load each (the rows are streamed once per step), a
 //     wave reads RPW = 64/LPR rows per load and U loads of K and of V per
@@ -229,6 +231,49 @@ struct AttendCore {
             for (int j = 0; j < G; ++j)
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) acc[j][e] = __builtin_fmaf(sc[u][j], vf[e], acc[j][e]);
+        }
+    }
+
+    // Loads this lane's rows of one iteration given their row units.
+    __device__ __forceinline__ void load_rows(const uint32_t *rid, const T *k_pool,
+                                              const T *v_pool, uint4 *kr, uint4 *vr,
+                                              bool *ok) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            ok[u] = rid[u] != kBadRow;
+            const int64_t off = (int64_t)(ok[u] ? rid[u] : 0u) * D + sub * EPL;
+            const u32x4 kz = ok[u] ? __builtin_nontemporal_load((const u32x4 *)(k_pool + off)) : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 vz = ok[u] ? __builtin_nontemporal_load((const u32x4 *)(v_pool + off)) : u32x4{0u, 0u, 0u, 0u};
+            kr[u] = make_uint4(kz.x, kz.y, kz.z, kz.w);
+            vr[u] = make_uint4(vz.x, vz.y, vz.z, vz.w);
+        }
+    }
+
+    // Streams rows [0, nrows) whose row units rowfn(f) gives (kBadRow for a
+    // row that does not exist).  The row units of the next iteration are
+    // resolved while this iteration's loads are in flight, so no row table
+    // (and no block barrier after building one) is needed.
+    template <typename RowFn>
+    __device__ __forceinline__ void stream_fn(int nrows, const T *k_pool, const T *v_pool,
+                                              RowFn rowfn) {
+        const int step = NW * ROWS_IT;
+        uint32_t rid[U];
+        int base = w * ROWS_IT;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int f = base + u * RPW + rsub;
+            rid[u] = f < nrows ? rowfn(f) : kBadRow;
+        }
+        for (; base < nrows; base += step) {
+            uint4 kr[U], vr[U];
+            bool ok[U];
+            load_rows(rid, k_pool, v_pool, kr, vr, ok);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int f = base + step + u * RPW + rsub;
+                rid[u] = f < nrows ? rowfn(f) : kBadRow;
+            }
+            consume(kr, vr, ok);
         }
     }
 

@@ -79,8 +79,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     constexpr int kBlock = NW * kWave;
     using Core = AttendCore<T, D, G, NW, 2, false>;
     constexpr size_t kKeyBytes = sizeof(uint64_t) * kFusedMaxPages;
-    constexpr size_t kRowBytes = sizeof(uint32_t) * kFusedMaxRows;
-    constexpr size_t kUnion = cmax(cmax(kStageBytes, kKeyBytes), kRowBytes);
+    constexpr size_t kUnion = cmax(kStageBytes, kKeyBytes);
     __shared__ float qs[G][D];
     __shared__ float qsel[G][D];
     __shared__ __align__(16) float qpm_s[D * 2 * G];
@@ -95,15 +94,14 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     __shared__ uint32_t hist[256];
     __shared__ int wave_tot[NW];
     __shared__ int sh[2];
-    // staged summaries or page keys (selection), then the row table
-    // (attention): never live at the same time
+    // staged summaries or page keys (selection): never live at the same
+    // time
     __shared__ __align__(16) unsigned char u_s[kUnion];
     T *stage = (T *)u_s;
     uint64_t *comp_s = (uint64_t *)u_s;
-    uint32_t *row_s = (uint32_t *)u_s;
     // the waves' partial attention states have LDS of their own, so a wave
     // stores its state as soon as its own rows are done while other waves
-    // still read the row table
+    // still stream
     __shared__ typename Core::Shared csh;
 
     const int sp = SPLIT ? blockIdx.x : 0, nsp = SPLIT ? gridDim.x : 1;
@@ -184,8 +182,31 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             report(a.status, RKV_DEV_BLOCK);
         }
     };
+    // bf16 with 32 channels and up to 512 pages: the staged rows sit at a
+    // fixed stride of 512 pages, so the bound loop (unrolled over the 32
+    // channels) reads LDS at constant offsets with no address arithmetic
+    constexpr int kSR = kWave * V;
+    const bool fixed = kPacked && staged && k1 == 32 && NP <= kSR && max_pages % V == 0 &&
+                       (((uintptr_t)sm_max) & 15u) == 0 && (((uintptr_t)sm_min) & 15u) == 0;
     if (staged) {
-        const int npad = stage_summaries<T, kBlock>(sm_max, sm_min, max_pages, 0, NP, ch_s, k1, stage);
+        int npad;
+        if (fixed) {
+            // one wave per summary row: row r (the max rows of the k1
+            // channels, then the min rows) lands at stage + r * kSR, lane l's
+            // 16-byte chunk at l * V within it
+            const int lane = tid & (kWave - 1), nv = (NP + V - 1) / V;
+            for (int row = tid / kWave; row < 2 * k1; row += NW) {
+                const int kind = row >= k1, i = row - kind * k1;
+                if (lane < nv) {
+                    const T *src = (kind ? sm_min : sm_max) + (int64_t)ch_s[i] * max_pages + lane * V;
+                    lds_load16_nt(src, stage + row * kSR);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            npad = kSR;
+        } else {
+            npad = stage_summaries<T, kBlock>(sm_max, sm_min, max_pages, 0, NP, ch_s, k1, stage);
+        }
         if (tid < NP) blk_s[tid] = pt;
         if (append && tid < D) {
             T nmax, nmin;
@@ -208,7 +229,8 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         if (tid < NP) {
             float sc;
             if constexpr (kPacked)
-                sc = staged_bound_exact<G>((const uint16_t *)stage, npad, tid, k1, qpm_s);
+                sc = fixed ? staged_bound_fixed<G, 32, kSR>((const uint16_t *)stage, tid, qpm_s)
+                           : staged_bound_exact<G>((const uint16_t *)stage, npad, tid, k1, qpm_s);
             else
                 sc = staged_bound<T, D, G>(stage, npad, tid, k1, qsel);
             skey = ordered_key(sc);
@@ -242,28 +264,33 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         lds_barrier();
         topk_ascending<kBlock>(comp_s, NP, K, cnt_s, hist, sh, wave_tot, emit);
     }
-    lds_barrier();
+    Core core;
+    core.init_lds(qs, a.qscale);
+    // The full barrier makes the page list visible and the appended K/V row
+    // (a global store of this block) visible to every wave before any of
+    // them reads it.
+    __syncthreads();
     RKV_STAMP(tid == 0, 4);
 
-    // 5. resolve the rows of the selected pages, then stream them.  The full
-    //    barrier makes the appended K/V row (a global store of this block)
-    //    visible to every wave before any of them reads it.
+    // 5. stream the rows of the selected pages; each wave resolves its own
+    //    rows from the page list as it goes.
     // (split-K: this block's share of the page list, pages [i0, i1))
     const int i0 = SPLIT ? min(K, sp * a.pps) : 0, i1 = SPLIT ? min(K, i0 + a.pps) : K;
     const int nrows = (i1 - i0) * P;
-    for (int f = tid; f < nrows; f += kBlock) {
-        const int pi = i0 + f / P, slot = f - (f / P) * P;
-        const int32_t pg = sel_s[pi];
-        uint32_t r = kBadRow;
-        if ((int64_t)pg * P + slot < n) {
-            const int32_t blk = blk_s[pg];
-            if (blk >= 0 && blk < a.num_blocks)
-                r = (uint32_t)(((int64_t)blk * a.Hkv + h) * P + slot);
-            else if (slot == 0)
-                report(a.status, RKV_DEV_BLOCK);
-        }
-        row_s[f] = r;
+    for (int o = tid; o < i1 - i0; o += kBlock) {
+        const int32_t blk = blk_s[sel_s[i0 + o]];
+        if (blk < 0 || blk >= a.num_blocks) report(a.status, RKV_DEV_BLOCK);
     }
+    // page size a power of two: shifts instead of divisions
+    const int pshift = (P & (P - 1)) == 0 ? __builtin_ctz(P) : -1;
+    auto rowfn = [&](int f) -> uint32_t {
+        const int pi = pshift >= 0 ? f >> pshift : f / P;
+        const int sl = f - pi * P;
+        const int32_t pg = sel_s[i0 + pi];
+        const int32_t blk = blk_s[pg];
+        if ((int64_t)pg * P + sl >= n || blk < 0 || blk >= a.num_blocks) return kBadRow;
+        return (uint32_t)(((int64_t)blk * a.Hkv + h) * P + sl);
+    };
     if constexpr (SPLIT) {
         // the lead block's store of the appended row may land after this
         // block reads it, so a block whose share holds that row writes the
@@ -279,11 +306,9 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             }
         }
     }
-    Core core;
-    core.init_lds(qs, a.qscale);
-    __syncthreads();
+    if constexpr (SPLIT) __syncthreads();  // the row written just above
     RKV_STAMP(tid == 0, 5);
-    core.stream(row_s, nrows, k_pool, v_pool);
+    core.stream_fn(nrows, k_pool, v_pool, rowfn);
     RKV_STAMP((tid & (kWave - 1)) == 0, 6 + tid / kWave);
     core.to_shared(csh);
     lds_barrier();
@@ -346,10 +371,10 @@ bool dispatch_g(int B, int nsp, const rkv_gqa &g, const DecArgs &a, const void *
 }
 
 // Split-K shape: about `target` blocks in all, whole pages per split, and at
-// most kFusedMaxRows rows per split (a block's row table).  The default
-// target is kSplitBlocks; selections of more than kSplitBlocks * 512 rows
-// in all (a stream that is bandwidth work, not latency) take one block per
-// CU instead.
+// most kFusedMaxRows rows per split (the stream share one block takes on).
+// The default target is kSplitBlocks; selections of more than
+// kSplitBlocks * 512 rows in all (a stream that is bandwidth work, not
+// latency) take one block per CU instead.
 void split_counts(int units, int k2, int P, int target, int &n_splits, int &pages_per_split) {
     if (target <= 0)
         target = (int64_t)units * k2 * P > (int64_t)kSplitBlocks * 512 ? kSplitBlocksWide
@@ -372,8 +397,9 @@ FusedPlan plan_fused(const rkv_gqa &g, int dtype, int B, int P, int max_pages, i
     const int block = fused_waves(g.group) * kWave;
     if (max_pages > kFusedMaxPages || P > kFusedMaxRows) return p;
     const int units = B * g.n_kv_heads;
-    // one block per unit holds every selected row in its row table; split-K
-    // blocks hold only their share, so larger selections split further
+    // one block per unit streams every selected row, at most kFusedMaxRows
+    // (the range this form is tested on); split-K blocks stream only their
+    // share, so larger selections split further
     const bool rows_fit = (int64_t)k2 * P <= kFusedMaxRows;
     // split-K needs the staged selection (every page's summaries in LDS),
     // else each of its blocks would read the summaries from memory

@@ -407,6 +407,14 @@ __device__ __forceinline__ void dma_copy_i32(const int32_t *src, int n, int32_t 
             __builtin_amdgcn_global_load_lds(src + base + lane, (lds_void *)(dst + base), 4, 0, 0);
 }
 
+// One 16-byte direct global-to-LDS load per lane: the calling wave's
+// lanes land at consecutive 16-byte slots from dst (wave-uniform).
+// Non-temporal (cache policy 2).
+__device__ __forceinline__ void lds_load16_nt(const void *src, void *dst) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 2);
+}
+
 template <typename T, int BLOCK>
 __device__ __forceinline__ int stage_summaries(const T *smax, const T *smin, int max_pages, int p0,
                                                int n, const int *ch_s, int k1, T *stage) {
@@ -481,6 +489,51 @@ __device__ __forceinline__ float staged_bound_exact(const uint16_t *stage, int n
         const float hv = __uint_as_float((uint32_t)hi_row[(int64_t)i * npad] << 16);
         const float lv = __uint_as_float((uint32_t)lo_row[(int64_t)i * npad] << 16);
         const float *qi = qpm + i * 2 * G;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            s[j] = __builtin_fmaf(qi[j], hv, s[j]);
+            s[j] = __builtin_fmaf(qi[G + j], lv, s[j]);
+        }
+    }
+    float tot = 0.0f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) tot = tot + s[j];
+    return tot;
+}
+
+// staged_bound_exact (same arithmetic and order) for K1 channels staged
+// with the fixed row stride SR: every LDS offset is a constant, so the
+// unrolled loop spends no instructions on addresses.
+template <int G, int K1, int SR>
+__device__ __forceinline__ float staged_bound_fixed(const uint16_t *stage, int p, const float *qpm) {
+    float s[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) s[j] = 0.0f;
+    const uint16_t *hi_row = stage + p;
+    const uint16_t *lo_row = stage + K1 * SR + p;
+    // the query table's address in a vector register (an opaque zero), so
+    // its reads take constant offsets from one base
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    const float *qb = (const float *)__builtin_assume_aligned((const char *)qpm + z, 16);
+#pragma unroll
+    for (int i = 0; i < K1; ++i) {
+        const float hv = __uint_as_float((uint32_t)hi_row[i * SR] << 16);
+        const float lv = __uint_as_float((uint32_t)lo_row[i * SR] << 16);
+        float qi[2 * G];
+        if constexpr ((2 * G) % 4 == 0) {
+#pragma unroll
+            for (int u = 0; u < 2 * G / 4; ++u) {
+                const float4 v4 = ((const float4 *)qb)[i * (2 * G / 4) + u];
+                qi[4 * u] = v4.x;
+                qi[4 * u + 1] = v4.y;
+                qi[4 * u + 2] = v4.z;
+                qi[4 * u + 3] = v4.w;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 2 * G; ++u) qi[u] = qb[i * 2 * G + u];
+        }
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             s[j] = __builtin_fmaf(qi[j], hv, s[j]);

@@ -24,7 +24,7 @@ from . import build, rkv, workloads
 from .session import Session
 
 PHASES = [("q + new row", 0, 1), ("channels", 1, 2), ("staging + fold", 2, 3),
-          ("page bounds", 3, 24), ("page top-k", 24, 4), ("row table", 4, 5)]
+          ("page bounds", 3, 24), ("page top-k", 24, 4), ("stream setup", 4, 5)]
 
 
 def wall_clock_khz(dev: int = 0) -> int:
