@@ -210,10 +210,15 @@ __global__ void __launch_bounds__(kSelBlock) select_kernel(SelArgs a, const T *q
             stage[(int64_t)(k1 + tid) * npad + pi] = ovr_lo[c];
         }
         lds_barrier();
+        // a full chunk of 256 pages with 32 channels: the row stride is the
+        // constant 256, so the unrolled bound reads LDS at constant offsets
+        const bool fixed = npad == kSortedChunk && k1 == 32 &&
+                           (size_t)2 * 32 * kSortedChunk * sizeof(T) <= (size_t)kStageCap;
         for (int pi = tid; pi < cnt; pi += kSelBlock) {
             float s;
             if constexpr (kPacked)
-                s = staged_bound_exact<G>((const uint16_t *)stage, npad, pi, k1, qpm_s);
+                s = fixed ? staged_bound_fixed<G, 32, kSortedChunk>((const uint16_t *)stage, pi, qpm_s)
+                          : staged_bound_exact<G>((const uint16_t *)stage, npad, pi, k1, qpm_s);
             else
                 s = staged_bound<T, D, G>(stage, npad, pi, k1, qsel);
             comp_s[pi] = composite_key(ordered_key(s), pi);
