@@ -155,6 +155,20 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[E], int n, int K
             cnt_T = cnt;
         }
     }
+    if (cnt_T == K) {
+        // exactly K keys are >= T (T > 0 whenever the search moved it, and
+        // every key when K = n), so they are the top K: no tie handling
+        int base = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (e * kWave >= n) break;
+            const bool sel = e * kWave + lane < n && key[e] >= T;
+            const uint64_t sm = __ballot(sel);
+            if (sel) emit(base + __popcll(sm & below), e * kWave + lane);
+            base += __popcll(sm);
+        }
+        return;
+    }
     int gt_tot = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) gt_tot += __popcll(__ballot(key[e] > T));
