@@ -51,6 +51,13 @@ DECODE_CASES = [
     # token-level selection (page 1) with k2 above 1,024, up to the limit
     (BF16, 1, 2, 4, 128, 1, 32, 2000, [5000], 5100),
     (F32, 1, 1, 2, 64, 1, 8, 4096, [4500], 4600),
+    # the fixed-stride staging of 32 channels at its edges: exactly 512
+    # pages (staged at the fixed stride), 513 pages (summaries read from
+    # memory), and a page capacity that is not a multiple of 8 (staged at
+    # the packed stride)
+    (BF16, 2, 2, 4, 128, 16, 32, 64, [8192, 8100], 520),
+    (BF16, 1, 2, 4, 128, 16, 32, 64, [8193], 520),
+    (BF16, 1, 2, 4, 128, 16, 32, 64, [3000], 190),
 ]
 
 
