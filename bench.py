@@ -77,6 +77,35 @@ def measured_copy_gbs(dev, nbytes: int = 1 << 30, reps: int = 5) -> float:
     return gbs
 
 
+def measured_read_gbs(dev, nbytes: int = 2 << 30, reps: int = 5) -> tuple[float, float]:
+    """The library's read probe over a 2 GiB buffer (eight times the 256 MB
+    last-level cache): a plain stream of every 4 KB chunk, and a gather of
+    half of them in a seeded random order (4 KB page slices at scattered
+    offsets, the decode kernel's K/V pattern).  Returns both rates, GB/s."""
+    import torch
+    from sparse_kv_cache_hsa_amd import rkv
+    chunk = rkv.RKV_READ_PROBE_CHUNK
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(rkv.RKV_READ_PROBE_SINK_WORDS, dtype=torch.int32, device=dev)
+    n = nbytes // chunk
+    g = torch.Generator().manual_seed(0)
+    offsets = (torch.randperm(n, generator=g)[: n // 2] * chunk).to(dev)
+    rates = []
+    for offs, nread in ((None, n * chunk), (offsets, (n // 2) * chunk)):
+        rkv.rkv_read_probe(buf, sink, offs)  # warm-up; checks the offsets
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            rkv.rkv_read_probe(buf, sink, offs, check_offsets=False)
+        e1.record()
+        torch.cuda.synchronize()
+        rates.append(reps * nread / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf, sink, offsets
+    torch.cuda.empty_cache()
+    return rates[0], rates[1]
+
+
 def counted_traffic(kernel: str, workload: str, build_id: str):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none for
@@ -507,6 +536,9 @@ def main():
 
     copy_gbs = measured_copy_gbs(dev)
     log(f"[bench] measured device copy (1 GiB, read + write): {copy_gbs:.0f} GB/s")
+    read_gbs, gather_gbs = measured_read_gbs(dev)
+    log(f"[bench] measured read probe (2 GiB): stream {read_gbs:.0f} GB/s, "
+        f"4 KB gather {gather_gbs:.0f} GB/s")
 
     steps_per_s = 1e3 / ms_step
     result = {
@@ -541,6 +573,10 @@ def main():
                      "traffic": traffic, "avg_launch_us": round(launch_us, 3),
                      "measured_copy_gbs": round(copy_gbs, 1),
                      "frac_of_measured_copy": round(kern_gbs / copy_gbs, 4),
+                     "measured_read_gbs": round(read_gbs, 1),
+                     "frac_of_measured_read": round(kern_gbs / read_gbs, 4),
+                     "measured_gather_gbs": round(gather_gbs, 1),
+                     "frac_of_measured_gather": round(kern_gbs / gather_gbs, 4),
                      "bytes_per_launch": int(bytes_launch)},
     }
     if turn_report:

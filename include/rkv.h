@@ -434,6 +434,26 @@ int rkv_decode_step_static(const rkv_gqa *g, int32_t dtype, int32_t B, const voi
                            float *page_scores, void *stream, const rkv_opts *opts);
 
 #ifdef __cplusplus
+/* ---- measurement helper (not part of the method) ---------------------- */
+/* Reads n_chunks chunks of RKV_READ_PROBE_CHUNK bytes from the device buffer
+ * buf (16-byte aligned) with 16-byte non-temporal loads, over at most
+ * RKV_READ_PROBE_BLOCKS blocks of 256 threads, and stores per wave the XOR
+ * of the 32-bit words it read into sink (device uint32; the first
+ * min(n_chunks, RKV_READ_PROBE_BLOCKS) * 4 words are written, at most
+ * RKV_READ_PROBE_SINK_WORDS), so no load can be dropped and the stored words
+ * XOR to the XOR of every word read.  Chunk i starts at byte offsets[i]
+ * (device int64; each a multiple of 16 with the chunk inside buf: device
+ * data, not checked) or, with offsets NULL, at i * RKV_READ_PROBE_CHUNK (buf
+ * then holds n_chunks chunks).  Asynchronous on stream.  It times the
+ * device's plain streaming read and its 4 KB page-slice gather (the decode
+ * kernel's K/V access pattern) beside the decode kernel.
+ * RKV_EINVAL: buf or sink NULL, buf not 16-byte aligned, or n_chunks < 1. */
+#define RKV_READ_PROBE_CHUNK 4096
+#define RKV_READ_PROBE_BLOCKS 2048
+#define RKV_READ_PROBE_SINK_WORDS (RKV_READ_PROBE_BLOCKS * 4)
+int rkv_read_probe(const void *buf, const int64_t *offsets, int64_t n_chunks, uint32_t *sink,
+                   void *stream);
+
 } /* extern "C" */
 #endif
 

@@ -210,12 +210,18 @@ struct AttendCore {
             for (int u = 0; u < U; ++u)
                 if (ok[u]) mx = fmaxf(mx, sc[u][j]);
             mx = rows_max<LPR>(mx);
-            const float mn = fmaxf(m[j], mx);
-            const float corr = exp2_diff(m[j], mn);
-            m[j] = mn;
-            float lj = l[j] * corr;
+            // Rescale only when the running maximum rises (it is uniform
+            // across the wave, so this is a uniform branch): otherwise the
+            // factor would be exp2(0) = 1 exactly, and the state unchanged.
+            if (mx > m[j]) {
+                const float corr = exp2_diff(m[j], mx);
+                m[j] = mx;
+                l[j] *= corr;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[j][e] *= corr;
+                for (int e = 0; e < EPL; ++e) acc[j][e] *= corr;
+            }
+            const float mn = m[j];
+            float lj = l[j];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 sc[u][j] = ok[u] ? fast_exp2(sc[u][j] - mn) : 0.0f;

@@ -37,6 +37,9 @@ RKV_FORM_SPLITK = 3
 RKV_DEV_LENGTH = 1
 RKV_DEV_BLOCK = 2
 RKV_DEV_PAGE = 4
+RKV_READ_PROBE_CHUNK = 4096
+RKV_READ_PROBE_BLOCKS = 2048
+RKV_READ_PROBE_SINK_WORDS = RKV_READ_PROBE_BLOCKS * 4
 
 EXPORTED = (
     "rkv_status_string", "rkv_build_id", "rkv_split_ratio",
@@ -44,7 +47,7 @@ EXPORTED = (
     "rkv_hsa_workspace_bytes", "rkv_hsa_select", "rkv_hsa_attend", "rkv_hsa_decode",
     "rkv_decode_step", "rkv_prefill_evict_chunk_workspace_bytes", "rkv_prefill_evict_chunk",
     "rkv_decode_mode", "rkv_decode_step_static", "rkv_turn_filter_workspace_bytes",
-    "rkv_turn_filter",
+    "rkv_turn_filter", "rkv_read_probe",
 )
 
 
@@ -155,6 +158,8 @@ def load_library(path: str | None = None, check_build_id: bool = True):
         lib.rkv_decode_step_static.argtypes = [G, i32, i32, vp, vp, vp, C, vp, vp, i32, i32, f32,
                                                vp, vp, vp, vp, vp, O]
         lib.rkv_decode_step_static.restype = ctypes.c_int
+        lib.rkv_read_probe.argtypes = [vp, vp, i64, vp, vp]
+        lib.rkv_read_probe.restype = ctypes.c_int
         if check_build_id:
             built = lib.rkv_build_id().decode()
             want = _build.source_hash()
@@ -517,3 +522,35 @@ def rkv_decode_step_static(g: rkv_gqa, q: torch.Tensor, k_new: torch.Tensor | No
         _ptr(v_new), ctypes.byref(cs), seq_lens.data_ptr(), summaries.data_ptr(), int(k1),
         int(k2), float(scale), out.data_ptr(), _ptr(chan_idx), _ptr(page_idx),
         _ptr(page_scores), _stream(), _opt(opts)))
+
+
+def rkv_read_probe(buf: torch.Tensor, sink: torch.Tensor, offsets: torch.Tensor | None = None,
+                   n_chunks: int | None = None, check_offsets: bool = True) -> None:
+    """Measurement helper: reads RKV_READ_PROBE_CHUNK-byte chunks of buf (a
+    device tensor, consecutive chunks, or the ones starting at the int64
+    byte offsets) and stores per-wave XORs of the words read into sink
+    (uint32 words as an int32 tensor of RKV_READ_PROBE_SINK_WORDS).  The
+    library does not check device offsets; check_offsets does it here (a
+    host synchronisation: pass False inside a timed loop once a call with
+    the same offsets has checked them)."""
+    if not buf.is_cuda or not sink.is_cuda:
+        raise ValueError("rkv_read_probe: buf and sink must be device tensors")
+    if sink.dtype != torch.int32 or sink.numel() < RKV_READ_PROBE_SINK_WORDS:
+        raise ValueError("rkv_read_probe: sink must be int32 with RKV_READ_PROBE_SINK_WORDS words")
+    nbytes = buf.numel() * buf.element_size()
+    if offsets is not None:
+        _need(offsets, "offsets", torch.int64)
+        n = offsets.numel() if n_chunks is None else int(n_chunks)
+        if n > offsets.numel():
+            raise ValueError("rkv_read_probe: more chunks than offsets")
+        if check_offsets and n > 0:
+            o = offsets[:n]
+            bad = ((o < 0) | (o % 16 != 0) | (o + RKV_READ_PROBE_CHUNK > nbytes)).any()
+            if bool(bad.item()):
+                raise ValueError("rkv_read_probe: an offset is unaligned or its chunk leaves buf")
+    else:
+        n = nbytes // RKV_READ_PROBE_CHUNK if n_chunks is None else int(n_chunks)
+        if n * RKV_READ_PROBE_CHUNK > nbytes:
+            raise ValueError("rkv_read_probe: buf holds fewer chunks than asked for")
+    _check("rkv_read_probe", load_library().rkv_read_probe(
+        buf.data_ptr(), _ptr(offsets), n, sink.data_ptr(), _stream()))

@@ -251,3 +251,15 @@ def test_turn_filter_argument_checks(rkv_lib):
     assert call([200], [40], stride=10) == L.RKV_EINVAL    # kept_idx row too short
     assert call([200], [40], ws=100) == L.RKV_EWORKSPACE
     assert L.rkv_turn_filter_workspace_bytes(g, 1, 320, 8) > 0
+
+
+def test_read_probe_argument_checks(rkv_lib):
+    """The read probe rejects a null buffer or sink, an unaligned buffer and
+    an empty read on the host, before any launch (the pointers below are
+    never dereferenced)."""
+    L = rkv_lib.load_library()
+    sink = ctypes.c_void_p(4096)
+    assert L.rkv_read_probe(None, None, 1, sink, None) == rkv_lib.RKV_EINVAL
+    assert L.rkv_read_probe(ctypes.c_void_p(4096), None, 1, None, None) == rkv_lib.RKV_EINVAL
+    assert L.rkv_read_probe(ctypes.c_void_p(4100), None, 1, sink, None) == rkv_lib.RKV_EINVAL
+    assert L.rkv_read_probe(ctypes.c_void_p(4096), None, 0, sink, None) == rkv_lib.RKV_EINVAL
