@@ -79,7 +79,9 @@ typedef struct rkv_gqa {
  * Logical row r of sequence b, KV head h lives at
  *   pool[page_table[b][r / page_size]][h][r % page_size][:].
  * The page size is also HSA's page: summaries and page selection are per
- * logical page.  Pools must be 16-byte aligned. */
+ * logical page.  Pools must be 16-byte aligned, and num_blocks * Hkv *
+ * page_size must be below 2^32 - 1 (the kernels name a pool row with 32
+ * bits; larger pools give RKV_EUNSUPPORTED). */
 typedef struct rkv_paged_cache {
     void *k_pool;
     void *v_pool;

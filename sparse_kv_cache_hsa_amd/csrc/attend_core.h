@@ -176,6 +176,8 @@ struct AttendCore {
         }
     }
 
+    // ALL: every row of the iteration exists (ok[] is then not read).
+    template <bool ALL = false>
     __device__ __forceinline__ void consume(const uint4 *kr, const uint4 *vr, const bool *ok) {
         float sc[U][G];
 #pragma unroll
@@ -208,7 +210,7 @@ struct AttendCore {
             float mx = -INFINITY;
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (ok[u]) mx = fmaxf(mx, sc[u][j]);
+                if (ALL || ok[u]) mx = fmaxf(mx, sc[u][j]);
             mx = rows_max<LPR>(mx);
             // Rescale only when the running maximum rises (it is uniform
             // across the wave, so this is a uniform branch): otherwise the
@@ -224,7 +226,7 @@ struct AttendCore {
             float lj = l[j];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                sc[u][j] = ok[u] ? fast_exp2(sc[u][j] - mn) : 0.0f;
+                sc[u][j] = (ALL || ok[u]) ? fast_exp2(sc[u][j] - mn) : 0.0f;
                 lj += sc[u][j];
             }
             l[j] = lj;
@@ -255,6 +257,19 @@ struct AttendCore {
         }
     }
 
+    // load_rows when every row unit is valid: no masks.
+    __device__ __forceinline__ void load_rows_all(const uint32_t *rid, const T *k_pool,
+                                                  const T *v_pool, uint4 *kr, uint4 *vr) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t off = (int64_t)rid[u] * D + sub * EPL;
+            const u32x4 kz = __builtin_nontemporal_load((const u32x4 *)(k_pool + off));
+            const u32x4 vz = __builtin_nontemporal_load((const u32x4 *)(v_pool + off));
+            kr[u] = make_uint4(kz.x, kz.y, kz.z, kz.w);
+            vr[u] = make_uint4(vz.x, vz.y, vz.z, vz.w);
+        }
+    }
+
     // Streams rows [0, nrows) whose row units rowfn(f) gives (kBadRow for a
     // row that does not exist).  The row units of the next iteration are
     // resolved while this iteration's loads are in flight, so no row table
@@ -273,7 +288,18 @@ struct AttendCore {
         for (; base < nrows; base += step) {
             uint4 kr[U], vr[U];
             bool ok[U];
-            load_rows(rid, k_pool, v_pool, kr, vr, ok);
+            bool mine = true;
+#pragma unroll
+            for (int u = 0; u < U; ++u) mine &= rid[u] != kBadRow;
+            // the usual iteration: every row of the wave exists (a uniform
+            // branch), so loads and softmax need no per-row masks
+            if (__ballot(!mine) == 0ull) {
+                load_rows_all(rid, k_pool, v_pool, kr, vr);
+#pragma unroll
+                for (int u = 0; u < U; ++u) ok[u] = true;
+            } else {
+                load_rows(rid, k_pool, v_pool, kr, vr, ok);
+            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int f = base + step + u * RPW + rsub;

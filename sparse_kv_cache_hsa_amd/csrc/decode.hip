@@ -281,15 +281,23 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
         const int32_t blk = blk_s[sel_s[i0 + o]];
         if (blk < 0 || blk >= a.num_blocks) report(a.status, RKV_DEV_BLOCK);
     }
-    // page size a power of two: shifts instead of divisions
+    // page size a power of two: shifts instead of divisions; row units in
+    // 32 bits (the pool holds fewer than 2^32 rows)
     const int pshift = (P & (P - 1)) == 0 ? __builtin_ctz(P) : -1;
+    const uint32_t rows_per_blk = (uint32_t)(a.Hkv * P), row_h = (uint32_t)(h * P);
     auto rowfn = [&](int f) -> uint32_t {
-        const int pi = pshift >= 0 ? f >> pshift : f / P;
-        const int sl = f - pi * P;
+        int pi, sl;
+        if (pshift >= 0) {
+            pi = f >> pshift;
+            sl = f & (P - 1);
+        } else {
+            pi = f / P;
+            sl = f - pi * P;
+        }
         const int32_t pg = sel_s[i0 + pi];
         const int32_t blk = blk_s[pg];
         if ((int64_t)pg * P + sl >= n || blk < 0 || blk >= a.num_blocks) return kBadRow;
-        return (uint32_t)(((int64_t)blk * a.Hkv + h) * P + sl);
+        return (uint32_t)blk * rows_per_blk + row_h + (uint32_t)sl;
     };
     if constexpr (SPLIT) {
         // the lead block's store of the appended row may land after this

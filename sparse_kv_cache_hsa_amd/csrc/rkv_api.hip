@@ -35,10 +35,15 @@ int check_dtype(int dtype) {
     return (dtype == RKV_F32 || dtype == RKV_BF16) ? RKV_OK : RKV_EUNSUPPORTED;
 }
 
-int check_cache(const rkv_paged_cache *c) {
+// g has passed check_gqa.
+int check_cache(const rkv_gqa *g, const rkv_paged_cache *c) {
     if (!c || !c->k_pool || !c->v_pool || !c->page_table) return RKV_EINVAL;
     if (c->num_blocks < 1 || c->page_size < 1 || c->max_pages < 1) return RKV_EINVAL;
     if (c->page_size > 256) return RKV_EUNSUPPORTED;
+    // the kernels name a pool row by a 32-bit unit (block * Hkv + head) * P
+    // + slot, with 0xffffffff reserved for "no row"
+    if (c->num_blocks > ((int64_t)0xffffffff - 1) / ((int64_t)g->n_kv_heads * c->page_size))
+        return RKV_EUNSUPPORTED;
     if ((int64_t)c->max_pages * c->page_size > (int64_t)1 << 30) return RKV_EINVAL;
     if (!aligned16(c->k_pool) || !aligned16(c->v_pool)) return RKV_EINVAL;
     return RKV_OK;
@@ -159,7 +164,7 @@ int rkv_prefill_evict(const rkv_gqa *g, int32_t dtype, int32_t B, const int32_t 
         return RKV_EINVAL;
     if (!(scale > 0.0f) || !isfinite(scale)) return RKV_EINVAL;
     if (!aligned16(k) || !aligned16(v)) return RKV_EINVAL;
-    if ((st = check_cache(cache)) != RKV_OK) return st;
+    if ((st = check_cache(g, cache)) != RKV_OK) return st;
     EvictSeq seq;
     memset(&seq, 0, sizeof seq);
     int64_t keep_rows = 0;
@@ -207,7 +212,7 @@ int rkv_prefill_evict_chunk(const rkv_gqa *g, int32_t dtype, int32_t B,
         return RKV_EINVAL;
     if (!(scale > 0.0f) || !isfinite(scale)) return RKV_EINVAL;
     if (!aligned16(k_chunk) || !aligned16(v_chunk)) return RKV_EINVAL;
-    if ((st = check_cache(cache)) != RKV_OK) return st;
+    if ((st = check_cache(g, cache)) != RKV_OK) return st;
     const int64_t cap = (int64_t)cache->max_pages * cache->page_size;
     ChunkSeq cs;
     EvictSeq seq;
@@ -258,8 +263,8 @@ int rkv_turn_filter(const rkv_gqa *g, int32_t dtype, int32_t B, const int32_t *n
     if (B > RKV_MAX_EVICT_BATCH) return RKV_EUNSUPPORTED;
     if (w < 1 || pool_kernel < 1 || (pool_kernel % 2) == 0) return RKV_EINVAL;
     if (!(scale > 0.0f) || !isfinite(scale)) return RKV_EINVAL;
-    if ((st = check_cache(full)) != RKV_OK) return st;
-    if ((st = check_cache(view)) != RKV_OK) return st;
+    if ((st = check_cache(g, full)) != RKV_OK) return st;
+    if ((st = check_cache(g, view)) != RKV_OK) return st;
     const int64_t cap_full = (int64_t)full->max_pages * full->page_size;
     const int64_t cap_view = (int64_t)view->max_pages * view->page_size;
     ChunkSeq cs;
@@ -300,7 +305,7 @@ int rkv_append_summaries(const rkv_gqa *g, int32_t dtype, int32_t B,
     if ((st = check_dtype(dtype)) != RKV_OK) return st;
     if (B < 1 || B > 65535 || !n_old || !n_new || !summaries || max_new_rows < 1)
         return RKV_EINVAL;
-    if ((st = check_cache(cache)) != RKV_OK) return st;
+    if ((st = check_cache(g, cache)) != RKV_OK) return st;
     if ((k_src == nullptr) != (v_src == nullptr)) return RKV_EINVAL;
     const int64_t pages = (int64_t)(max_new_rows + cache->page_size - 1) / cache->page_size + 1;
     if (pages > 0x7fffffff) return RKV_EINVAL;
@@ -340,7 +345,7 @@ int rkv_hsa_attend(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
     clear_pending_error();
     int st = check_gqa(g);
     if (st != RKV_OK) return st;
-    if ((st = check_cache(cache)) != RKV_OK) return st;
+    if ((st = check_cache(g, cache)) != RKV_OK) return st;
     st = check_select_args(g, dtype, B, q, seq_lens, cache->page_size, cache->max_pages, 1, k2);
     if (st != RKV_OK) return st;
     if (!page_idx || !out || !(scale > 0.0f) || !isfinite(scale)) return RKV_EINVAL;
@@ -371,7 +376,7 @@ int rkv_decode_step(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
     clear_pending_error();
     int st = check_gqa(g);
     if (st != RKV_OK) return st;
-    if ((st = check_cache(cache)) != RKV_OK) return st;
+    if ((st = check_cache(g, cache)) != RKV_OK) return st;
     st = check_select_args(g, dtype, B, q, seq_lens, cache->page_size, cache->max_pages, k1, k2);
     if (st != RKV_OK) return st;
     if (!summaries || !out || !(scale > 0.0f) || !isfinite(scale)) return RKV_EINVAL;
@@ -405,7 +410,7 @@ int rkv_decode_step_static(const rkv_gqa *g, int32_t dtype, int32_t B, const voi
     clear_pending_error();
     int st = check_gqa(g);
     if (st != RKV_OK) return st;
-    if ((st = check_cache(cache)) != RKV_OK) return st;
+    if ((st = check_cache(g, cache)) != RKV_OK) return st;
     st = check_select_args(g, dtype, B, q, seq_lens, cache->page_size, cache->max_pages, k1, k2);
     if (st != RKV_OK) return st;
     const size_t need = hsa_ws(*g, B, cache->page_size, cache->max_pages, k2, knobs_of(opts)).total;

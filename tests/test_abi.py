@@ -48,9 +48,9 @@ def test_split_rejects_bad_ratio(rkv_lib):
 
 
 def _call_decode(lib, g, dtype=0, B=1, P=16, max_pages=8, k1=8, k2=4, scale=0.125,
-                 ws_bytes=1 << 20, null_q=False, null_out=False):
+                 ws_bytes=1 << 20, null_q=False, null_out=False, num_blocks=64):
     fake = 0x10000  # never dereferenced: every case below fails a host check
-    cache = lib.rkv_paged_cache(fake, fake, fake, 64, P, max_pages)
+    cache = lib.rkv_paged_cache(fake, fake, fake, num_blocks, P, max_pages)
     return lib.load_library().rkv_hsa_decode(
         ctypes.byref(g) if g is not None else None, dtype, B, None if null_q else fake,
         ctypes.byref(cache), fake, fake, k1, k2, scale, None if null_out else fake,
@@ -76,6 +76,10 @@ def test_decode_argument_checks(rkv_lib):
     assert _call_decode(L, g, null_q=True) == L.RKV_EINVAL
     assert _call_decode(L, g, null_out=True) == L.RKV_EINVAL
     assert _call_decode(L, g, ws_bytes=16) == L.RKV_EWORKSPACE
+    # a pool of 2^32 - 1 rows or more: the kernels' 32-bit row units
+    # cannot name its rows (8 heads x 16 rows per block)
+    assert _call_decode(L, g, num_blocks=(0xFFFFFFFF - 1) // 128 + 1) == L.RKV_EUNSUPPORTED
+    assert _call_decode(L, g, num_blocks=(0xFFFFFFFF - 1) // 128, ws_bytes=16) == L.RKV_EWORKSPACE
 
 
 def test_workspace_sizes(rkv_lib):
