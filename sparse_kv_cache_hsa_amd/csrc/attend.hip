@@ -66,7 +66,10 @@ attend_kernel(AttArgs a, const T *k_pool, const T *v_pool, const T *q) {
     Core core;
     core.init(q, bh, a.qscale);
     __syncthreads();
-    core.stream(row_s, nrows, k_pool, v_pool);
+    if constexpr (PIPE)
+        core.stream(row_s, nrows, k_pool, v_pool);
+    else
+        core.stream_fn(nrows, k_pool, v_pool, [&](int f) { return row_s[f]; });
     core.to_shared(sh);
     __syncthreads();
     if (a.n_splits == 1) {
