@@ -29,7 +29,7 @@ namespace rkv {
 namespace {
 
 constexpr int kTK = 64;      // keys per logits tile
-constexpr int kCH = 512;     // keys per denominator chunk
+constexpr int kCH = 256;     // keys per denominator chunk
 constexpr int kLogitsBlock = 128;
 
 struct EvictWs {
@@ -371,10 +371,12 @@ colsum_kernel(int Hkv, int G, int w, int64_t L_max, EvictSeq seq, const float *Z
     A[bh * L_max + t] = a;
 }
 
-// Column sums for R <= 128 (at most 34 KB of LDS): a block takes 64 prefix keys; its threads compute
-// p = expf(z - m) / ell for whole Z rows (coalesced over r) into LDS, then one
-// thread per key adds them over i, then j, in the definition's order.
-constexpr int kCsKeys = 64;
+// Column sums for R <= 128: a block takes 32 prefix keys (at most 17 KB of
+// LDS, so eight blocks share a CU and hide each other's load round trips);
+// its threads compute p = expf(z - m) / ell for whole Z rows (coalesced over
+// r) into LDS, then one thread per key adds them over i, then j, in the
+// definition's order.
+constexpr int kCsKeys = 32;
 
 __global__ void __launch_bounds__(256)
 colsum_tiled_kernel(int Hkv, int G, int w, int64_t L_max, EvictSeq seq, const float *Z,
