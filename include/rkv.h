@@ -388,8 +388,8 @@ int rkv_hsa_decode(const rkv_gqa *g, int32_t dtype, int32_t B, const void *q,
  *     kernel, one 16-wave block per (sequence, KV head);
  *   - otherwise, when the summaries fit the kernel's LDS stage (max_pages <=
  *     1024, 512 for G = 8, and 2 * k1 * max_pages * sizeof(element) <= 64 KiB,
- *     max_pages
- *     rounded up to 16 bytes of elements): the same kernel split K-wise,
+ *     max_pages rounded up to 16 bytes of elements): the same kernel split
+ *     K-wise,
  *     about 128 blocks in all (256 when more than 65,536 rows are selected
  *     in all, more when a share would exceed 2048 rows),
  *     each making the unit's selection and attending to a share of its

@@ -309,34 +309,29 @@ struct AttendCore {
         }
     }
 
-    // Streams rows [0, nrows) of row_s (visible to the block).
+    // Streams rows [0, nrows) of row_s (visible to the block), double
+    // buffered: each wave issues its next iteration's loads before it
+    // consumes the current rows (the pipelined attention variants; the
+    // others use stream_fn).
     __device__ __forceinline__ void stream(const uint32_t *row_s, int nrows, const T *k_pool,
                                            const T *v_pool) {
+        static_assert(PIPE, "the unpipelined form streams through stream_fn");
         const int step = NW * ROWS_IT;
-        if constexpr (PIPE) {
-            uint4 kn[U], vn[U];
-            bool okn[U];
-            int base = w * ROWS_IT;
-            issue(row_s, nrows, k_pool, v_pool, base, kn, vn, okn);
-            for (; base < nrows; base += step) {
-                uint4 kr[U], vr[U];
-                bool ok[U];
+        uint4 kn[U], vn[U];
+        bool okn[U];
+        int base = w * ROWS_IT;
+        issue(row_s, nrows, k_pool, v_pool, base, kn, vn, okn);
+        for (; base < nrows; base += step) {
+            uint4 kr[U], vr[U];
+            bool ok[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    kr[u] = kn[u];
-                    vr[u] = vn[u];
-                    ok[u] = okn[u];
-                }
-                if (base + step < nrows) issue(row_s, nrows, k_pool, v_pool, base + step, kn, vn, okn);
-                consume(kr, vr, ok);
+            for (int u = 0; u < U; ++u) {
+                kr[u] = kn[u];
+                vr[u] = vn[u];
+                ok[u] = okn[u];
             }
-        } else {
-            for (int base = w * ROWS_IT; base < nrows; base += step) {
-                uint4 kr[U], vr[U];
-                bool ok[U];
-                issue(row_s, nrows, k_pool, v_pool, base, kr, vr, ok);
-                consume(kr, vr, ok);
-            }
+            if (base + step < nrows) issue(row_s, nrows, k_pool, v_pool, base + step, kn, vn, okn);
+            consume(kr, vr, ok);
         }
     }
 
