@@ -73,14 +73,17 @@ attend_kernel(AttArgs a, const T *k_pool, const T *v_pool, const T *q) {
     core.to_shared(sh);
     __syncthreads();
     if (a.n_splits == 1) {
-        Core::combine(sh, [&](int j, int c, float M, float Ls, float A) {
-            a.out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
+        Core::combine(sh, [&](int j, int c, float M, float Ls, float A0, float A1) {
+            float *o = a.out + (bh * G + j) * D + c;
+            o[0] = Ls > 0.0f ? A0 / Ls : 0.0f;
+            o[1] = Ls > 0.0f ? A1 / Ls : 0.0f;
         });
     } else {
         float *base = a.part + (bh * a.n_splits + sp) * G * (D + 2);
-        Core::combine(sh, [&](int j, int c, float M, float Ls, float A) {
+        Core::combine(sh, [&](int j, int c, float M, float Ls, float A0, float A1) {
             float *pp = base + j * (D + 2);
-            pp[c] = A;
+            pp[c] = A0;
+            pp[c + 1] = A1;
             if (c == 0) {
                 pp[D] = M;
                 pp[D + 1] = Ls;

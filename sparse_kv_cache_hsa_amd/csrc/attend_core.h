@@ -91,7 +91,7 @@ struct AttendCore {
     static constexpr int RPW = kWave / LPR;  // rows per wave load
     static constexpr int ROWS_IT = U * RPW;  // rows per wave iteration
 
-    struct Shared {
+    struct alignas(16) Shared {
         float wm[NW][G], wl[NW][G];
         float wacc[NW][G][D];
     };
@@ -351,38 +351,83 @@ struct AttendCore {
         }
     }
 
+    // With four row groups of 16 lanes, four values are summed over the row
+    // groups with three lane swaps: a 16-lane swap of (a, b) and of (c, d)
+    // gives rows {a01, b01, a23, b23} and {c01, d01, c23, d23} (xy = the sum
+    // of rows x and y, lower row first), and a 32-lane swap of those two
+    // gives the totals of a, b, c and d in rows 0..3, added in the same
+    // order as pair sums over 16 and then 32 lanes.
+    static __device__ __forceinline__ float sum4_rows(float a, float b, float c, float d) {
+        const auto ab = __builtin_amdgcn_permlane16_swap((int)__float_as_uint(a),
+                                                         (int)__float_as_uint(b), false, false);
+        const auto cd = __builtin_amdgcn_permlane16_swap((int)__float_as_uint(c),
+                                                         (int)__float_as_uint(d), false, false);
+        const float t = __uint_as_float((uint32_t)ab[0]) + __uint_as_float((uint32_t)ab[1]);
+        const float u = __uint_as_float((uint32_t)cd[0]) + __uint_as_float((uint32_t)cd[1]);
+        const auto tu = __builtin_amdgcn_permlane32_swap((int)__float_as_uint(t),
+                                                         (int)__float_as_uint(u), false, false);
+        return __uint_as_float((uint32_t)tu[0]) + __uint_as_float((uint32_t)tu[1]);
+    }
+
     __device__ __forceinline__ void to_shared(Shared &sh) {
-        merge_groups<LPR>();
-        if (rsub == 0) {
+        if constexpr (LPR == 16 && G % 4 == 0) {
+            // row group r of lane ends with head 4*hg + r's totals: its EPL
+            // channels, then its softmax sum
 #pragma unroll
-            for (int j = 0; j < G; ++j) {
-                if (sub == 0) {
-                    sh.wm[w][j] = m[j];
-                    sh.wl[w][j] = l[j];
+            for (int hg = 0; hg < G / 4; ++hg) {
+                float tot[EPL];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e)
+                    tot[e] = sum4_rows(acc[4 * hg][e], acc[4 * hg + 1][e], acc[4 * hg + 2][e],
+                                       acc[4 * hg + 3][e]);
+                const float lt = sum4_rows(l[4 * hg], l[4 * hg + 1], l[4 * hg + 2], l[4 * hg + 3]);
+                const int j = 4 * hg + rsub;
+                float4 *dst = (float4 *)&sh.wacc[w][j][sub * EPL];
+#pragma unroll
+                for (int e = 0; e < EPL; e += 4)
+                    dst[e / 4] = make_float4(tot[e], tot[e + 1], tot[e + 2], tot[e + 3]);
+                if (sub == 0) sh.wl[w][j] = lt;
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int j = 0; j < G; ++j) sh.wm[w][j] = m[j];
+            }
+        } else {
+            merge_groups<LPR>();
+            if (rsub == 0) {
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    if (sub == 0) {
+                        sh.wm[w][j] = m[j];
+                        sh.wl[w][j] = l[j];
+                    }
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) sh.wacc[w][j][sub * EPL + e] = acc[j][e];
                 }
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) sh.wacc[w][j][sub * EPL + e] = acc[j][e];
             }
         }
     }
 
-    // Combines the waves in wave order: fn(j, c, max, sum, acc) once per
-    // (head, channel) across the block.
+    // Combines the waves in wave order: fn(j, c, max, sum, acc_c, acc_c+1)
+    // once per (head, channel pair) across the block.
     template <typename Fn>
     static __device__ __forceinline__ void combine(const Shared &sh, Fn fn) {
-        for (int t = threadIdx.x; t < G * D; t += NW * kWave) {
-            const int j = t / D, c = t % D;
+        static_assert(D % 2 == 0, "channel pairs");
+        for (int t = threadIdx.x; t < G * D / 2; t += NW * kWave) {
+            const int j = t / (D / 2), c = 2 * (t % (D / 2));
             float M = -INFINITY;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sh.wm[ww][j]);
-            float Ls = 0.0f, A = 0.0f;
+            float Ls = 0.0f, A0 = 0.0f, A1 = 0.0f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) {
                 const float cw = exp2_diff(sh.wm[ww][j], M);
+                const float2 x = *(const float2 *)&sh.wacc[ww][j][c];
                 Ls += sh.wl[ww][j] * cw;
-                A += sh.wacc[ww][j][c] * cw;
+                A0 += x.x * cw;
+                A1 += x.y * cw;
             }
-            fn(j, c, M, Ls, A);
+            fn(j, c, M, Ls, A0, A1);
         }
     }
 };

@@ -322,17 +322,20 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     lds_barrier();
     if constexpr (SPLIT) {
         float *base = a.part + (bh * nsp + sp) * G * (D + 2);
-        Core::combine(csh, [&](int j, int c, float M, float Ls, float A) {
+        Core::combine(csh, [&](int j, int c, float M, float Ls, float A0, float A1) {
             float *pp = base + j * (D + 2);
-            pp[c] = A;
+            pp[c] = A0;
+            pp[c + 1] = A1;
             if (c == 0) {
                 pp[D] = M;
                 pp[D + 1] = Ls;
             }
         });
     } else {
-        Core::combine(csh, [&](int j, int c, float M, float Ls, float A) {
-            a.out[(bh * G + j) * D + c] = Ls > 0.0f ? A / Ls : 0.0f;
+        Core::combine(csh, [&](int j, int c, float M, float Ls, float A0, float A1) {
+            float *o = a.out + (bh * G + j) * D + c;
+            o[0] = Ls > 0.0f ? A0 / Ls : 0.0f;
+            o[1] = Ls > 0.0f ? A1 / Ls : 0.0f;
         });
     }
     // the page list goes out last: stored earlier, it would hold up the full
