@@ -58,8 +58,9 @@ DECODE_CASES = [
     (BF16, 2, 2, 4, 128, 16, 32, 64, [8192, 8100], 520),
     (BF16, 1, 2, 4, 128, 16, 32, 64, [8193], 520),
     (BF16, 1, 2, 4, 128, 16, 32, 64, [3000], 190),
-    # bf16 at head_dim 128 with groups of 1 and 2 query heads (the query
-    # rows of the matrix-core q.k padded with zero heads), ragged rows
+    # bf16 at head_dim 128 with groups of 1 and 2 query heads (the
+    # attention merge's per-head lane sums; groups of 4 and 8 take the
+    # four-heads-per-swap form), ragged rows
     (BF16, 2, 2, 1, 128, 16, 32, 32, [700, 333], 64),
     (BF16, 3, 2, 2, 128, 8, 16, 24, [900, 17, 260], 128),
 ]
