@@ -170,14 +170,18 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
             nmin = fx < Elem<T>::ld(&omin, 0) ? xv : omin;
         }
     };
+    // The kernel's own results (the appended row and summary, the output, the
+    // page list) are stored non-temporally: each is written once, and only the
+    // appended row may be read again in this launch, once, by the stream
+    // (measurably faster).
     auto store_append = [&](T nmax, T nmin) {
         const int32_t blk = blk_s[p_new];
         if (lead && blk >= 0 && blk < a.num_blocks) {
             const int64_t dst = (((int64_t)blk * a.Hkv + h) * P + slot) * D + tid;
-            k_pool[dst] = x;
-            v_pool[dst] = vx;
-            sm_max[im] = nmax;
-            sm_min[im] = nmin;
+            __builtin_nontemporal_store(x, &k_pool[dst]);
+            __builtin_nontemporal_store(vx, &v_pool[dst]);
+            __builtin_nontemporal_store(nmax, &sm_max[im]);
+            __builtin_nontemporal_store(nmin, &sm_min[im]);
         } else if (lead && tid == 0) {
             report(a.status, RKV_DEV_BLOCK);
         }
@@ -334,14 +338,15 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     } else {
         Core::combine(csh, [&](int j, int c, float M, float Ls, float A0, float A1) {
             float *o = a.out + (bh * G + j) * D + c;
-            o[0] = Ls > 0.0f ? A0 / Ls : 0.0f;
-            o[1] = Ls > 0.0f ? A1 / Ls : 0.0f;
+            __builtin_nontemporal_store(Ls > 0.0f ? A0 / Ls : 0.0f, &o[0]);
+            __builtin_nontemporal_store(Ls > 0.0f ? A1 / Ls : 0.0f, &o[1]);
         });
     }
     // the page list goes out last: stored earlier, it would hold up the full
     // barrier before the stream (which waits for this wave's stores)
     if (a.page_out && lead)
-        for (int o = tid; o < k2; o += kBlock) a.page_out[bh * k2 + o] = o < K ? sel_s[o] : -1;
+        for (int o = tid; o < k2; o += kBlock)
+            __builtin_nontemporal_store(o < K ? sel_s[o] : -1, &a.page_out[bh * k2 + o]);
 #ifdef RKV_PHASE_TIMING
     lds_barrier();
     RKV_STAMP(tid == 0, 22);
