@@ -285,7 +285,22 @@ struct AttendCore {
             const int f = base + u * RPW + rsub;
             rid[u] = f < nrows ? rowfn(f) : kBadRow;
         }
-        for (; base < nrows; base += step) {
+        // The SIMDs serve their waves oldest first, so the youngest wave of
+        // each SIMD finishes its (equal) share last.  A wave's issue priority
+        // steps down 3 -> 0 as it gets through the quarters of its share, so
+        // a wave that is behind outranks one that is ahead (measurably
+        // faster; the rows and their order are unchanged, so are the bits).
+        const int n_it = base < nrows ? (nrows - base + step - 1) / step : 0;
+        int lvl = 0;
+        __builtin_amdgcn_s_setprio(3);
+        for (int it = 0; base < nrows; base += step, ++it) {
+            const int nl = (4 * it >= n_it) + (4 * it >= 2 * n_it) + (4 * it >= 3 * n_it);
+            if (nl != lvl) {
+                lvl = nl;
+                if (lvl == 1) __builtin_amdgcn_s_setprio(2);
+                else if (lvl == 2) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+            }
             uint4 kr[U], vr[U];
             bool ok[U];
             bool mine = true;
@@ -307,6 +322,7 @@ struct AttendCore {
             }
             consume(kr, vr, ok);
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 
     // Streams rows [0, nrows) of row_s (visible to the block), double
