@@ -274,26 +274,50 @@ struct AttendCore {
     // row that does not exist).  The row units of the next iteration are
     // resolved while this iteration's loads are in flight, so no row table
     // (and no block barrier after building one) is needed.
-    template <typename RowFn>
+    //
+    // Iterations of ROWS_IT rows go to the waves round-robin (OLDER_PCT = 0)
+    // or, for a block whose waves w and w + NW/2 share a SIMD, in contiguous
+    // ranges: each such pair of waves takes an equal range, of which the
+    // older wave (w < NW/2, which the SIMD serves first) takes the first
+    // OLDER_PCT percent.  Either way the split depends only on nrows, so the
+    // rows of a wave and their order, hence the bits, do not depend on timing.
+    template <int OLDER_PCT = 0, typename RowFn>
     __device__ __forceinline__ void stream_fn(int nrows, const T *k_pool, const T *v_pool,
                                               RowFn rowfn) {
-        const int step = NW * ROWS_IT;
+        static_assert(OLDER_PCT == 0 || (NW % 2 == 0 && OLDER_PCT > 0 && OLDER_PCT < 100),
+                      "wave pairs");
+        int it0, n_it, stride;
+        if constexpr (OLDER_PCT == 0) {
+            const int T_it = (nrows + ROWS_IT - 1) / ROWS_IT;
+            it0 = w;
+            n_it = w < T_it ? (T_it - w + NW - 1) / NW : 0;
+            stride = NW;
+        } else {
+            const int T_it = (nrows + ROWS_IT - 1) / ROWS_IT;
+            const int half = NW / 2, pr = w % half;
+            const int p0 = (int)((int64_t)T_it * pr / half);
+            const int p1 = (int)((int64_t)T_it * (pr + 1) / half);
+            const int cut = p0 + ((p1 - p0) * OLDER_PCT + 50) / 100;
+            it0 = w < half ? p0 : cut;
+            n_it = w < half ? cut - p0 : p1 - cut;
+            stride = 1;
+        }
+        const int step = stride * ROWS_IT;
         uint32_t rid[U];
-        int base = w * ROWS_IT;
+        int base = it0 * ROWS_IT;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int f = base + u * RPW + rsub;
-            rid[u] = f < nrows ? rowfn(f) : kBadRow;
+            rid[u] = n_it > 0 && f < nrows ? rowfn(f) : kBadRow;
         }
-        // The SIMDs serve their waves oldest first, so the youngest wave of
-        // each SIMD finishes its (equal) share last.  A wave's issue priority
+        // The SIMDs serve their waves oldest first, so of equal shares the
+        // youngest wave of each SIMD finishes last.  A wave's issue priority
         // steps down 3 -> 0 as it gets through the quarters of its share, so
         // a wave that is behind outranks one that is ahead (measurably
-        // faster; the rows and their order are unchanged, so are the bits).
-        const int n_it = base < nrows ? (nrows - base + step - 1) / step : 0;
+        // faster; scheduling only, the bits are unchanged).
         int lvl = 0;
         __builtin_amdgcn_s_setprio(3);
-        for (int it = 0; base < nrows; base += step, ++it) {
+        for (int it = 0; it < n_it; base += step, ++it) {
             const int nl = (4 * it >= n_it) + (4 * it >= 2 * n_it) + (4 * it >= 3 * n_it);
             if (nl != lvl) {
                 lvl = nl;
@@ -318,7 +342,7 @@ struct AttendCore {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int f = base + step + u * RPW + rsub;
-                rid[u] = f < nrows ? rowfn(f) : kBadRow;
+                rid[u] = it + 1 < n_it && f < nrows ? rowfn(f) : kBadRow;
             }
             consume(kr, vr, ok);
         }

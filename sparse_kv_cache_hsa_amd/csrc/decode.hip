@@ -78,9 +78,9 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
               T *summ) {
     constexpr int kBlock = NW * kWave;
     // The stream runs on the first half of the waves (the two oldest of
-    // each SIMD, which the SIMD serves first) with four rows per lane per
-    // iteration: as many bytes in flight as sixteen waves with two rows,
-    // with two age tiers to wait for instead of four (measurably faster).
+    // each SIMD) with four rows per lane per iteration: as many bytes in
+    // flight as sixteen waves with two rows, with two age tiers to balance
+    // instead of four (measurably faster).
     constexpr int NWS = NW == 16 ? 8 : NW;
     using Core = AttendCore<T, D, G, NWS, NW == 16 ? 4 : 2, false>;
     constexpr size_t kKeyBytes = sizeof(uint64_t) * kFusedMaxPages;
@@ -325,7 +325,9 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     }
     if constexpr (SPLIT) __syncthreads();  // the row written just above
     RKV_STAMP(tid == 0, 5);
-    if (tid < NWS * kWave) core.stream_fn(nrows, k_pool, v_pool, rowfn);
+    // (the older wave of each SIMD pair takes 56 % of their rows: the split
+    // at which both finish together, measured)
+    if (tid < NWS * kWave) core.template stream_fn<56>(nrows, k_pool, v_pool, rowfn);
     RKV_STAMP((tid & (kWave - 1)) == 0, 6 + tid / kWave);
     if (tid < NWS * kWave) core.to_shared(csh);
     lds_barrier();
