@@ -23,6 +23,7 @@ import torch
 from . import build, rkv, workloads
 from .session import Session
 
+STREAM_WAVES = 8
 PHASES = [("q + new row", 0, 1), ("channels", 1, 2), ("staging + fold", 2, 3),
           ("page bounds", 3, 24), ("page top-k", 24, 4), ("stream setup", 4, 5)]
 
@@ -47,7 +48,9 @@ def table(trace: np.ndarray, khz: int) -> dict:
     res = {"phases_mean_us": {}, "per_xcc": {}, "launch_span_us": {}}
     for name, a, b in PHASES:
         res["phases_mean_us"][name] = float((rel[:, :, b] - rel[:, :, a]).mean())
-    wave_end = rel[:, :, 6:22]
+    # the decode kernel streams on its first STREAM_WAVES waves; the others
+    # stamp their (empty) stream's end at once
+    wave_end = rel[:, :, 6:6 + STREAM_WAVES]
     res["phases_mean_us"]["stream, first wave"] = float((wave_end.min(2) - rel[:, :, 5]).mean())
     res["phases_mean_us"]["stream, last wave"] = float((wave_end.max(2) - rel[:, :, 5]).mean())
     res["phases_mean_us"]["merge + outputs"] = float((rel[:, :, 22] - wave_end.max(2)).mean())
