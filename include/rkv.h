@@ -143,8 +143,9 @@ typedef struct rkv_opts {
  * units of the device's constant wall clock (hipDeviceAttributeWallClockRate):
  * slot 0 block start, 1 queries loaded, 2 channels ranked, 3 summaries
  * staged, 24 page bounds done, 4 pages chosen and visible to the block, 5
- * stream starts, 6..21 the end of each of the 16 waves' streams, 22 block
- * end, 23 the XCC the block ran on; slots 25..31 are unused. */
+ * stream starts, 6..21 the end of each wave's stream (6 + wave; the stream
+ * runs on the first 8 waves, the others stamp at once), 22 block end, 23 the
+ * XCC the block ran on; slots 25..31 are unused. */
 #define RKV_TRACE_SLOTS 32
 
 /* Human-readable text for a status code (static storage). */

@@ -15,7 +15,8 @@
 //   - a row of d elements is read by LPR lanes with one 16-byte non-temporal
 //     load each (the rows are streamed once per step), a
 //     wave reads RPW = 64/LPR rows per load and U loads of K and of V per
-//     iteration; waves take iterations round-robin;
+//     iteration; waves take iterations round-robin, or (the fused decode
+//     kernel) in contiguous ranges sized by the waves' age on their SIMD;
 //   - each lane holds its EPL channels of the G query heads (the G heads share
 //     every K/V load) and an online-softmax state per head in the log2 domain
 //     (hardware exp2); the running maximum is kept uniform across the row
