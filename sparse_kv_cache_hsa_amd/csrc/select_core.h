@@ -138,7 +138,43 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[E], int n, int K
     // all (count(key > T) + count(key == T) = K).
     constexpr int GS = E < 4 ? E : 4;
     int cnt_T = n;  // count(key >= T)
-    for (int bit = top; bit >= 0 && cnt_T != K; --bit) {
+    int bit = top;
+    if constexpr (E <= 2) {
+        // few keys per lane: two bits per round, the three candidates of
+        // bits (bit, bit-1) counted together and the largest that keeps K
+        // keys taken (the same T as two one-bit rounds), which halves the
+        // chain of dependent rounds
+        for (; bit >= 1 && cnt_T != K; bit -= 2) {
+            const uint32_t c1 = T | (1u << (bit - 1)), c2 = T | (2u << (bit - 1)),
+                           c3 = T | (3u << (bit - 1));
+            uint64_t m1[E], m2[E], m3[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                m1[e] = __ballot(key[e] >= c1);
+                m2[e] = __ballot(key[e] >= c2);
+                m3[e] = __ballot(key[e] >= c3);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            int n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                n1 += __popcll(m1[e]);
+                n2 += __popcll(m2[e]);
+                n3 += __popcll(m3[e]);
+            }
+            if (n3 >= K) {
+                T = c3;
+                cnt_T = n3;
+            } else if (n2 >= K) {
+                T = c2;
+                cnt_T = n2;
+            } else if (n1 >= K) {
+                T = c1;
+                cnt_T = n1;
+            }
+        }
+    }
+    for (; bit >= 0 && cnt_T != K; --bit) {
         const uint32_t cand = T | (1u << bit);
         int cnt = 0;
 #pragma unroll
@@ -221,22 +257,32 @@ __device__ __forceinline__ void rank_channels_wave(const float (*qs)[D], int k1,
                                                    float (*qsel)[D], float *qpm = nullptr) {
     static_assert(D % kWave == 0, "head_dim");
     constexpr int E = D / kWave;
+    static_assert(E == 1 || E == 2, "head_dim 64 or 128");
     if (threadIdx.x < kWave) {
         const int lane = threadIdx.x;
+        // this lane's channels (lane, kWave + lane) of every head, kept for
+        // the emission: a lane emits only its own channels
+        float q0[G], q1[G];
         uint32_t key[E];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            q0[j] = qs[j][lane];
+            q1[j] = E == 2 ? qs[j][(E - 1) * kWave + lane] : 0.0f;
+        }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             float acc = 0.0f;
 #pragma unroll
-            for (int j = 0; j < G; ++j) acc = acc + fabsf(qs[j][e * kWave + lane]);
+            for (int j = 0; j < G; ++j) acc = acc + fabsf(e == 0 ? q0[j] : q1[j]);
             // acc >= +0, so its bits order like its value
             key[e] = __float_as_uint(acc);
         }
         wave_topk<E>(key, D, k1, [&](int o, int c) {
             ch_s[o] = c;
+            const bool second = c >= kWave;
 #pragma unroll
             for (int j = 0; j < G; ++j) {
-                const float qv = qs[j][c];
+                const float qv = second ? q1[j] : q0[j];
                 qsel[j][o] = qv;
                 if (qpm) {
                     // by sign bit, so -0 goes to the Kmin side (both sides
