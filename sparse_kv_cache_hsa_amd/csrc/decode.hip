@@ -90,7 +90,7 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     __shared__ __align__(16) float qpm_s[D * 2 * G];
     constexpr bool kPacked = std::is_same<T, uint16_t>::value;
     __shared__ int ch_s[D];
-    __shared__ T ovr_hi[D], ovr_lo[D], xs[D];
+    __shared__ T ovr_hi[D], ovr_lo[D];
     // the selected pages: K = min(k2, NP) <= max_pages <= kFusedMaxPages
     __shared__ int32_t sel_s[kFusedMaxPages];
     __shared__ int32_t blk_s[kFusedMaxPages];
@@ -136,7 +136,6 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     if (k_new != nullptr && tid < D) {
         x = k_new[bh * D + tid];
         vx = v_new[bh * D + tid];
-        xs[tid] = x;
     }
     RKV_STAMP(tid == 0, 0);
     load_group_q<T, D, G, kBlock>(q, bh, qs);
