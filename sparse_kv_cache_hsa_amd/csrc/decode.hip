@@ -285,10 +285,13 @@ decode_kernel(DecArgs a, const T *q, const T *k_new, const T *v_new, T *k_pool, 
     // (split-K: this block's share of the page list, pages [i0, i1))
     const int i0 = SPLIT ? min(K, sp * a.pps) : 0, i1 = SPLIT ? min(K, i0 + a.pps) : K;
     const int nrows = (i1 - i0) * P;
-    for (int o = tid; o < i1 - i0; o += kBlock) {
-        const int32_t blk = blk_s[sel_s[i0 + o]];
-        if (blk < 0 || blk >= a.num_blocks) report(a.status, RKV_DEV_BLOCK);
-    }
+    // (checked by the waves that do not stream, when there are such)
+    constexpr int kChk0 = NWS < NW ? NWS * kWave : 0;
+    if (tid >= kChk0)
+        for (int o = tid - kChk0; o < i1 - i0; o += kBlock - kChk0) {
+            const int32_t blk = blk_s[sel_s[i0 + o]];
+            if (blk < 0 || blk >= a.num_blocks) report(a.status, RKV_DEV_BLOCK);
+        }
     // page size a power of two: shifts instead of divisions; row units in
     // 32 bits (the pool holds fewer than 2^32 rows)
     const int pshift = (P & (P - 1)) == 0 ? __builtin_ctz(P) : -1;

@@ -100,7 +100,11 @@ __device__ __forceinline__ K wave_sort_desc(K key) {
 template <int E, typename Emit>
 __device__ __forceinline__ void wave_topk(const uint32_t (&key)[E], int n, int K, Emit emit) {
     const int lane = threadIdx.x & (kWave - 1);
-    const uint64_t below = lane ? (~0ull >> (kWave - lane)) : 0ull;
+    // lanes below this one among the set bits of a wave mask
+    auto below_cnt = [](uint64_t m) {
+        return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    };
     // The bits above the highest one in which two keys differ are common to
     // all of them, so T starts with them (wave-wide OR and AND of the keys;
     // the slots past n hold 0 and are left out of the AND).
@@ -200,7 +204,7 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[E], int n, int K
             if (e * kWave >= n) break;
             const bool sel = e * kWave + lane < n && key[e] >= T;
             const uint64_t sm = __ballot(sel);
-            if (sel) emit(base + __popcll(sm & below), e * kWave + lane);
+            if (sel) emit(base + below_cnt(sm), e * kWave + lane);
             base += __popcll(sm);
         }
         return;
@@ -216,9 +220,9 @@ __device__ __forceinline__ void wave_topk(const uint32_t (&key)[E], int n, int K
         const bool valid = e * kWave + lane < n;
         const bool eq = valid && key[e] == T;
         const uint64_t em = __ballot(eq);
-        const bool sel = (valid && key[e] > T) || (eq && eq_seen + __popcll(em & below) < take_eq);
+        const bool sel = (valid && key[e] > T) || (eq && eq_seen + below_cnt(em) < take_eq);
         const uint64_t sm = __ballot(sel);
-        if (sel) emit(base + __popcll(sm & below), e * kWave + lane);
+        if (sel) emit(base + below_cnt(sm), e * kWave + lane);
         base += __popcll(sm);
         eq_seen += __popcll(em);
     }
