@@ -205,6 +205,15 @@ __device__ void block_topk_emit(Load load, int n, uint32_t thr, int take_eq, int
 // 2^-126).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A store written through the caches to memory (a relaxed system-scope
+// atomic store: sc0 sc1 on gfx950).  Scattered small results of a kernel
+// stored this way leave no dirty L2 lines behind, which the end of the
+// launch would otherwise have to write back before the next kernel starts.
+template <typename T>
+__device__ __forceinline__ void store_through(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // The two values of lanes (lane & ~OFF, lane | OFF) of a 64-lane wave, for
 // OFF = 16 or 32, in every lane: `lo` from the lower lane, `hi` from the
 // upper one (the gfx950 lane-swap instructions, vector ALU only).
